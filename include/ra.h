@@ -1,0 +1,205 @@
+/*
+ * ra.h -- C ABI of libra.so: one rank's blockwise ring-attention step on an
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  Ring attention keeps each rank's block of queries fixed
+ * and passes key/value blocks around a ring until every query block has seen
+ * every key/value block it needs ("Sequence Parallelism III: Ring Attention for
+ * Context That Does Not Fit"; dictionary entry "context parallelism").  Each
+ * arriving block yields a partial output and its log-sum-exp (DeDLOC guide,
+ * "Step 3", local attention returning output and LSE), and partials are merged
+ * by log-sum-exp rescaling (DeDLOC guide, "3. Online Softmax Rescaling Across
+ * Decentralized Ranks").  Under a causal mask, blocks above the diagonal are
+ * skipped (DeDLOC guide, "Best Practices", row "Causal Mask Handling").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers.  Tensor pointers are HIP device pointers owned by the caller.  The
+ *   library never allocates, frees or synchronises; work is enqueued on the
+ *   caller's stream (`stream` is a hipStream_t passed as void*, NULL = the
+ *   null stream).  The caller keeps buffers alive until the stream completes.
+ * Layouts.  Contiguous, row-major:
+ *   q  [B, Sq, Hq,  D]   element type `dtype`
+ *   k  [B, Sk, Hkv, D]   element type `dtype`
+ *   v  [B, Sk, Hkv, D]   element type `dtype`
+ *   o  [B, Sq, Hq,  D]   float32, normalised output
+ *   lse[B, Sq, Hq]       float32, natural-log log-sum-exp of the scaled scores
+ *                        of each (row, head), in O's row order.
+ *   Query head h reads key/value head h / (Hq / Hkv) (consecutive grouping).
+ * Positions.  Rows of q and k are a rank's tokens in its local order.  Spans
+ *   give their global positions: local rows [off, off + len) of span i hold
+ *   global tokens [start, start + len), spans concatenated in order.  The
+ *   causal mask compares global positions: key j is visible to query i iff
+ *   j <= i.
+ * Empty rows.  A row that sees no key has the merge identity o = 0,
+ *   lse = -inf.  Merging with the identity returns the other side bit-exactly.
+ * Errors.  Every call returns RA_OK (0) or a negative status.  Arguments are
+ *   validated before anything is enqueued, so on error nothing was enqueued and
+ *   no output was touched; ra_last_error() describes the failure (thread-local
+ *   string, valid until the next call on the same thread).  RA_E_HIP reports
+ *   a failed kernel launch.
+ * Threading.  The library keeps no state between calls; calls are reentrant.
+ *   Calls that write the same output buffers must be ordered by the caller.
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RA_ABI_VERSION 1
+
+/* status codes */
+#define RA_OK 0
+#define RA_E_INVAL (-1)       /* bad shape, divisibility, null pointer or flag */
+#define RA_E_UNSUPPORTED (-2) /* dtype or head dimension not built            */
+#define RA_E_HIP (-3)         /* the HIP runtime refused a launch             */
+
+/* element types of q, k, v */
+#define RA_DTYPE_F32 0
+#define RA_DTYPE_BF16 1
+
+/* chunk-to-rank orders */
+#define RA_ORDER_CONTIGUOUS 0
+#define RA_ORDER_ZIGZAG 1
+
+/* ra_step flags */
+#define RA_STEP_INIT 0u  /* overwrite (o, lse) with this block's partial     */
+#define RA_STEP_ACCUM 1u /* merge this block's partial into (o, lse)         */
+
+/* ra_ulysses_relayout directions */
+#define RA_SEQ2HEAD 0
+#define RA_HEAD2SEQ 1
+
+/* classes of a (query span, key span) pair */
+#define RA_CLASS_SKIP 0 /* no pair visible                               */
+#define RA_CLASS_FULL 1 /* every pair visible                            */
+#define RA_CLASS_DIAG 2 /* some pairs visible: the diagonal needs a mask */
+
+typedef struct ra_span {
+  int64_t start; /* global position of the span's first token */
+  int64_t len;   /* number of tokens                          */
+} ra_span;
+
+/* One ring step: a rank's fixed query rows against one arrived K/V block. */
+typedef struct ra_step_desc {
+  int32_t dtype;    /* RA_DTYPE_F32 or RA_DTYPE_BF16                         */
+  int32_t B, Hq, Hkv, D;
+  int64_t Sq, Sk;   /* rows of q and of k/v; each = sum of its span lengths   */
+  int32_t causal;   /* 1: key j visible to query i iff j <= i; 0: all visible */
+  float scale;      /* score scale, normally 1/sqrt(D)                        */
+  int32_t n_qspans, n_kspans; /* 1 or 2 each                                  */
+  ra_span qspans[2], kspans[2];
+} ra_step_desc;
+
+/*
+ * ra_step -- one ring step (the per-step block computation of the DeDLOC
+ * guide, "Step 3", plus the merge of its section 3, fused).
+ *
+ * flags == RA_STEP_INIT: (o, lse) := this block's partial result; rows that
+ *   see no key of the block get (0, -inf).
+ * flags == RA_STEP_ACCUM: (o, lse) := merge((o, lse), partial).  Rows that see
+ *   no key are left untouched.
+ * Key tiles that the mask hides entirely are neither loaded nor computed.
+ * Requires: dtype/D in {F32: 64, 128; BF16: 64, 128}; Hq % Hkv == 0; spans of
+ * non-negative length whose lengths sum to Sq (Sk); 16-byte aligned q, k, v, o.
+ * Lengths need not be multiples of the kernel tiles.
+ */
+int ra_step(const ra_step_desc* d, const void* q, const void* k, const void* v,
+            float* o, float* lse, uint32_t flags, void* stream);
+
+/*
+ * ra_lse_merge -- merge two partial results of the same rows (DeDLOC guide,
+ * "3. Online Softmax Rescaling Across Decentralized Ranks"):
+ *   m = max(lse_a, lse_b), w_x = exp(lse_x - m),
+ *   o = (w_a o_a + w_b o_b) / (w_a + w_b),  lse = m + ln(w_a + w_b),
+ * with (0, -inf) as the exact identity.  o_* are [rows, D] float32, lse_* are
+ * [rows] float32.  o_out may alias o_a or o_b and lse_out may alias lse_a or
+ * lse_b (element-wise in place); other overlaps are not allowed.  rows >= 0
+ * (0 enqueues nothing), 1 <= D <= 4096.
+ */
+int ra_lse_merge(int64_t rows, int32_t D, const float* o_a, const float* lse_a,
+                 const float* o_b, const float* lse_b, float* o_out,
+                 float* lse_out, void* stream);
+
+/* One rank of a ring of P, all of whose K/V shards are resident. */
+typedef struct ra_rank_desc {
+  int32_t dtype;  /* RA_DTYPE_F32 or RA_DTYPE_BF16 */
+  int32_t B, Hq, Hkv, D;
+  int64_t S;      /* global sequence length */
+  int32_t P, rank;
+  int32_t order;  /* RA_ORDER_CONTIGUOUS or RA_ORDER_ZIGZAG */
+  int32_t causal;
+  float scale;
+} ra_rank_desc;
+
+/*
+ * ra_rank_forward -- rank `rank`'s P ring steps, run in ring order on one GPU.
+ * At step s the rank holds the shard of rank (rank - s) mod P (the static ring
+ * 0 -> 1 -> ... -> P-1 -> 0 of the DeDLOC guide, "The Geo-Distributed
+ * Long-Context Crisis").  Shards follow the chunk order: contiguous, rank r
+ * owns tokens [r S/P, (r+1) S/P); zigzag, the sequence is cut into 2P chunks
+ * and rank r owns chunk r then chunk 2P-1-r (ringmaster "Layout": contiguous
+ * shard and head_tail balancer; "Sequence Parallelism IV ... Load-Balanced
+ * Rings").
+ *   q_local  [B, S/P, Hq, D]       this rank's queries in its local order
+ *   k_shards [P, B, S/P, Hkv, D]   shard p in rank p's local order; v_shards same
+ *   o        [B, S/P, Hq, D] float32, lse [B, S/P, Hq] float32
+ * Equivalent to ra_step INIT at step 0 followed by ACCUM steps; a step whose
+ * whole block is masked is not launched.  Requires S % P == 0 (contiguous) or
+ * S % (2P) == 0 (zigzag), 0 <= rank < P, and ra_step's requirements.
+ */
+int ra_rank_forward(const ra_rank_desc* d, const void* q_local,
+                    const void* k_shards, const void* v_shards, float* o,
+                    float* lse, void* stream);
+
+/*
+ * ra_ulysses_relayout -- the local pack/unpack around the Ulysses all-to-all
+ * ("Sequence Parallelism II: DeepSpeed Ulysses and All-to-All Attention": a
+ * rank goes from all heads of its tokens to all tokens of a subset of heads).
+ * Destination j of P_u owns heads [j H/P_u, (j+1) H/P_u).
+ *   RA_SEQ2HEAD: in [B, s_loc, H, D] -> out [P_u, B, s_loc, H/P_u, D],
+ *                out[j, b, t, h', :] = in[b, t, j H/P_u + h', :]
+ *   RA_HEAD2SEQ: the exact inverse.
+ * A bit-exact permutation of elem_bytes-byte elements (1, 2, 4 or 8).
+ * Requires H % P_u == 0, P_u >= 1; in and out must not overlap.
+ */
+int ra_ulysses_relayout(int32_t dir, int32_t elem_bytes, int32_t B,
+                        int64_t s_loc, int32_t H, int32_t D, int32_t P_u,
+                        const void* in, void* out, void* stream);
+
+/* Host-side plan of one ring step (integers only, no GPU work). */
+typedef struct ra_plan_out {
+  int32_t src;                 /* rank whose shard is held at this step    */
+  int32_t n_qspans, n_kspans;
+  ra_span qspans[2], kspans[2];/* global spans, local order                */
+  int32_t pair_class[2][2];    /* RA_CLASS_* of (query span i, key span j) */
+  int64_t tiles_full, tiles_diag, tiles_skip; /* (tile_q x tile_k) tiles   */
+} ra_plan_out;
+
+/*
+ * ra_plan -- the index maps and mask classes behind ra_rank_forward, exposed
+ * so they can be checked exactly: the source shard of step `step`, both
+ * ranks' global spans, the class of each (query span, key span) pair, and the
+ * number of FULL / DIAG / SKIP tiles when query rows are cut into tiles of
+ * tile_q and key rows into tiles of tile_k (tiles restart at each span; the
+ * last tile of a span may be short).  Same requirements on (S, P, rank) as
+ * ra_rank_forward, 0 <= step < P, tile sizes >= 1.
+ */
+int ra_plan(int32_t order, int64_t S, int32_t P, int32_t rank, int32_t step,
+            int32_t causal, int32_t tile_q, int32_t tile_k, ra_plan_out* out);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* ra_last_error(void);
+
+/* RA_ABI_VERSION of the built library. */
+int ra_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

@@ -1,0 +1,273 @@
+"""Python binding of libra.so: one rank's blockwise ring-attention step on
+MI355X (gfx950).
+
+The functions here carry the C ABI's names and only marshal arguments: they
+check tensor devices, dtypes, shapes and contiguity, pass raw pointers and the
+current HIP stream, and raise ``RaError`` on a non-zero status.  Every step of
+the computation runs in the library's HIP kernels.  If libra.so is missing the
+import fails; build it with ``python -m ring_attention_blockwise_amd.build``.
+
+Layouts (see include/ra.h): q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D] in float32
+or bfloat16; o [B, Sq, Hq, D] float32; lse [B, Sq, Hq] float32 (natural log).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libra.so")
+
+RA_OK, RA_E_INVAL, RA_E_UNSUPPORTED, RA_E_HIP = 0, -1, -2, -3
+RA_DTYPE_F32, RA_DTYPE_BF16 = 0, 1
+RA_ORDER_CONTIGUOUS, RA_ORDER_ZIGZAG = 0, 1
+RA_STEP_INIT, RA_STEP_ACCUM = 0, 1
+RA_SEQ2HEAD, RA_HEAD2SEQ = 0, 1
+RA_CLASS_SKIP, RA_CLASS_FULL, RA_CLASS_DIAG = 0, 1, 2
+CLASS_NAMES = {RA_CLASS_SKIP: "SKIP", RA_CLASS_FULL: "FULL", RA_CLASS_DIAG: "DIAG"}
+ORDERS = {"contiguous": RA_ORDER_CONTIGUOUS, "zigzag": RA_ORDER_ZIGZAG}
+
+
+class RaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+class ra_span(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_int64), ("len", ctypes.c_int64)]
+
+
+class ra_step_desc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("Sq", ctypes.c_int64),
+                ("Sk", ctypes.c_int64), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("n_qspans", ctypes.c_int32), ("n_kspans", ctypes.c_int32),
+                ("qspans", ra_span * 2), ("kspans", ra_span * 2)]
+
+
+class ra_rank_desc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("S", ctypes.c_int64),
+                ("P", ctypes.c_int32), ("rank", ctypes.c_int32), ("order", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class ra_plan_out(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_int32), ("n_qspans", ctypes.c_int32), ("n_kspans", ctypes.c_int32),
+                ("qspans", ra_span * 2), ("kspans", ra_span * 2),
+                ("pair_class", (ctypes.c_int32 * 2) * 2),
+                ("tiles_full", ctypes.c_int64), ("tiles_diag", ctypes.c_int64),
+                ("tiles_skip", ctypes.c_int64)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m ring_attention_blockwise_amd.build`")
+# The library must share PyTorch's HIP runtime: torch hands it device pointers
+# and stream handles.  Both runtimes carry the soname libamdhip64.so.7, so
+# loading torch first makes the dynamic loader bind libra.so to torch's copy
+# instead of starting a second runtime from the system ROCm.
+try:
+    import torch as _torch_runtime  # noqa: F401
+except ImportError:  # pragma: no cover - host-only use (ra_plan) without torch
+    _torch_runtime = None
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32, _i64, _u32, _fp = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p
+lib.ra_step.argtypes = [ctypes.POINTER(ra_step_desc), _vp, _vp, _vp, _fp, _fp, _u32, _vp]
+lib.ra_lse_merge.argtypes = [_i64, _i32, _fp, _fp, _fp, _fp, _fp, _fp, _vp]
+lib.ra_rank_forward.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp, _fp, _fp, _vp]
+lib.ra_ulysses_relayout.argtypes = [_i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp]
+lib.ra_plan.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ra_plan_out)]
+lib.ra_last_error.restype = ctypes.c_char_p
+lib.ra_last_error.argtypes = []
+lib.ra_abi_version.restype = ctypes.c_int
+lib.ra_abi_version.argtypes = []
+for _f in ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_ulysses_relayout", "ra_plan"):
+    getattr(lib, _f).restype = ctypes.c_int
+
+EXPORTS = ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_ulysses_relayout", "ra_plan",
+           "ra_last_error", "ra_abi_version")
+
+
+def hip_runtime_path() -> str:
+    """Path of the libamdhip64 this process has loaded (one runtime expected)."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                paths.add(line.split()[-1])
+    return ";".join(sorted(paths))
+
+
+def ra_last_error() -> str:
+    return lib.ra_last_error().decode()
+
+
+def ra_abi_version() -> int:
+    return lib.ra_abi_version()
+
+
+def _check(status: int) -> None:
+    if status != RA_OK:
+        raise RaError(status, ra_last_error())
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return RA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return RA_DTYPE_BF16
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _require(t, name, dtype=None, ndim=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+
+
+def _spans(spans):
+    arr = (ra_span * 2)()
+    for i, (a, n) in enumerate(spans):
+        arr[i] = ra_span(int(a), int(n))
+    return arr
+
+
+def ra_step(q, k, v, o, lse, qspans, kspans, *, causal: bool, scale: float | None = None,
+            accum: bool = False, stream=None) -> None:
+    """One ring step: (o, lse) := partial (INIT) or merge((o, lse), partial) (ACCUM).
+
+    qspans/kspans: lists of (global start, length) of q's and k's rows, in
+    local order (at most two each).
+    """
+    torch = _torch()
+    _require(q, "q", ndim=4)
+    _require(k, "k", dtype=q.dtype, ndim=4)
+    _require(v, "v", dtype=q.dtype, ndim=4)
+    _require(o, "o", dtype=torch.float32, ndim=4)
+    _require(lse, "lse", dtype=torch.float32, ndim=3)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Sk, Hkv, D] matching q")
+    if tuple(o.shape) != (B, Sq, Hq, D) or tuple(lse.shape) != (B, Sq, Hq):
+        raise ValueError("o must be [B, Sq, Hq, D] and lse [B, Sq, Hq]")
+    d = ra_step_desc(_dtype_code(q), B, Hq, Hkv, D, Sq, Sk, 1 if causal else 0,
+                     float(scale if scale is not None else D ** -0.5), len(qspans), len(kspans),
+                     _spans(qspans), _spans(kspans))
+    _check(lib.ra_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                       RA_STEP_ACCUM if accum else RA_STEP_INIT, _stream(stream)))
+
+
+def ra_rank_forward(q_local, k_shards, v_shards, o, lse, *, S: int, P: int, rank: int, order: str,
+                    causal: bool, scale: float | None = None, stream=None) -> None:
+    """Rank ``rank``'s P ring steps.  q_local [B, S/P, Hq, D]; k_shards,
+    v_shards [P, B, S/P, Hkv, D] (shard p in rank p's local order); o and lse
+    are written."""
+    torch = _torch()
+    _require(q_local, "q_local", ndim=4)
+    _require(k_shards, "k_shards", dtype=q_local.dtype, ndim=5)
+    _require(v_shards, "v_shards", dtype=q_local.dtype, ndim=5)
+    _require(o, "o", dtype=torch.float32, ndim=4)
+    _require(lse, "lse", dtype=torch.float32, ndim=3)
+    B, s_loc, Hq, D = q_local.shape
+    Hkv = k_shards.shape[3]
+    if P * s_loc != S:
+        raise ValueError("q_local must hold S/P rows")
+    if tuple(k_shards.shape) != (P, B, s_loc, Hkv, D) or k_shards.shape != v_shards.shape:
+        raise ValueError("k_shards and v_shards must be [P, B, S/P, Hkv, D]")
+    if tuple(o.shape) != (B, s_loc, Hq, D) or tuple(lse.shape) != (B, s_loc, Hq):
+        raise ValueError("o must be [B, S/P, Hq, D] and lse [B, S/P, Hq]")
+    d = ra_rank_desc(_dtype_code(q_local), B, Hq, Hkv, D, S, P, rank, ORDERS[order],
+                     1 if causal else 0, float(scale if scale is not None else D ** -0.5))
+    _check(lib.ra_rank_forward(ctypes.byref(d), _ptr(q_local), _ptr(k_shards), _ptr(v_shards),
+                               _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def ra_lse_merge(o_a, lse_a, o_b, lse_b, o_out, lse_out, *, stream=None) -> None:
+    """Element-wise merge of two partials; o_* [..., D] and lse_* [...] float32.
+    o_out may be o_a or o_b (in place)."""
+    torch = _torch()
+    for t, n in ((o_a, "o_a"), (o_b, "o_b"), (o_out, "o_out"), (lse_a, "lse_a"), (lse_b, "lse_b"),
+                 (lse_out, "lse_out")):
+        _require(t, n, dtype=torch.float32)
+    D = o_a.shape[-1] if o_a.dim() else 0
+    rows = o_a.numel() // D if D else 0
+    if o_b.shape != o_a.shape or o_out.shape != o_a.shape:
+        raise ValueError("o_a, o_b, o_out must have the same shape")
+    for t in (lse_a, lse_b, lse_out):
+        if t.numel() != rows:
+            raise ValueError("lse tensors must hold one value per row of o")
+    _check(lib.ra_lse_merge(rows, D, _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b),
+                            _ptr(o_out), _ptr(lse_out), _stream(stream)))
+
+
+def ra_ulysses_relayout(x, out, P_u: int, direction: int = RA_SEQ2HEAD, *, stream=None) -> None:
+    """SEQ2HEAD: x [B, s_loc, H, D] -> out [P_u, B, s_loc, H/P_u, D];
+    HEAD2SEQ: x [P_u, B, s_loc, H/P_u, D] -> out [B, s_loc, H, D]."""
+    _require(x, "x")
+    _require(out, "out", dtype=x.dtype)
+    if direction == RA_SEQ2HEAD:
+        if x.dim() != 4:
+            raise ValueError("x must be [B, s_loc, H, D]")
+        B, s_loc, H, D = x.shape
+        want = (P_u, B, s_loc, H // P_u, D) if P_u > 0 and H % P_u == 0 else None
+    elif direction == RA_HEAD2SEQ:
+        if x.dim() != 5 or x.shape[0] != P_u:
+            raise ValueError("x must be [P_u, B, s_loc, H/P_u, D]")
+        _, B, s_loc, hp, D = x.shape
+        H = hp * P_u
+        want = (B, s_loc, H, D)
+    else:
+        raise ValueError("direction must be RA_SEQ2HEAD or RA_HEAD2SEQ")
+    if want is not None and tuple(out.shape) != want:
+        raise ValueError(f"out must have shape {want}")
+    _check(lib.ra_ulysses_relayout(direction, x.element_size(), B, s_loc, H, D, P_u, _ptr(x),
+                                   _ptr(out), _stream(stream)))
+
+
+def ra_plan(order: str, S: int, P: int, rank: int, step: int, causal: bool, tile_q: int,
+            tile_k: int) -> dict:
+    """Host plan of one ring step (no GPU work)."""
+    out = ra_plan_out()
+    _check(lib.ra_plan(ORDERS[order] if isinstance(order, str) else int(order), S, P, rank, step,
+                       1 if causal else 0, tile_q, tile_k, ctypes.byref(out)))
+    return {
+        "src": out.src,
+        "qspans": [(out.qspans[i].start, out.qspans[i].len) for i in range(out.n_qspans)],
+        "kspans": [(out.kspans[i].start, out.kspans[i].len) for i in range(out.n_kspans)],
+        "classes": [[CLASS_NAMES[out.pair_class[i][j]] for j in range(out.n_kspans)]
+                    for i in range(out.n_qspans)],
+        "tiles": {"FULL": out.tiles_full, "DIAG": out.tiles_diag, "SKIP": out.tiles_skip},
+    }
+
+
+def rank_spans(order: str, S: int, P: int, rank: int):
+    """Global spans of ``rank``'s rows, from the library's plan."""
+    return ra_plan(order, S, P, rank, 0, True, 1 << 30, 1 << 30)["qspans"]

@@ -1,0 +1,177 @@
+// Bandwidth-bound kernels: the standalone log-sum-exp merge of two partial
+// results, and the Ulysses sequence<->head regrouping.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Unsigned division by a run-time constant with a precomputed multiplier
+// (round-up method of Granlund & Montgomery, "Division by invariant integers
+// using multiplication", 1994): q = (umulhi(n, m) + n) >> s for n < 2^31.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  f.s = s;
+  f.m = (uint32_t)((((1ull << s) - d) << 32) / d + 1);
+  return f;
+}
+
+__device__ inline uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+// ---------------------------------------------------------------------------
+// Merge (DeDLOC guide, "3. Online Softmax Rescaling Across Decentralized
+// Ranks"): with m = max(lse_a, lse_b), w = exp(lse - m):
+//   o = (w_a o_a + w_b o_b) / (w_a + w_b), lse = m + ln(w_a + w_b),
+// and (0, -inf) passes the other side through unchanged.  One thread handles
+// V consecutive floats of one row (V = 4 when D % 4 == 0, else 1).
+template <int V>
+__global__ __launch_bounds__(256) void lse_merge_kernel(uint32_t total, FastDiv per_row, int D,
+                                                        const float* __restrict__ o_a,
+                                                        const float* __restrict__ lse_a,
+                                                        const float* __restrict__ o_b,
+                                                        const float* __restrict__ lse_b,
+                                                        float* o_out, float* lse_out) {
+  const uint32_t u = blockIdx.x * 256u + threadIdx.x;
+  if (u >= total) return;
+  const uint32_t row = fdiv(u, per_row);
+  const uint32_t col = (u - row * per_row.d) * V;
+  const float la = lse_a[row], lb = lse_b[row];
+  const long long off = (long long)row * D + col;
+  float ca, cb;
+  float lo;
+  if (la == kNegInf && lb == kNegInf) {
+    ca = 0.f; cb = 0.f; lo = kNegInf;
+  } else if (la == kNegInf) {
+    ca = 0.f; cb = 1.f; lo = lb;
+  } else if (lb == kNegInf) {
+    ca = 1.f; cb = 0.f; lo = la;
+  } else {
+    const float m = fmaxf(la, lb);
+    const float wa = __builtin_amdgcn_exp2f((la - m) * kLog2e);
+    const float wb = __builtin_amdgcn_exp2f((lb - m) * kLog2e);
+    const float den = wa + wb;
+    ca = wa / den;
+    cb = wb / den;
+    lo = m + __builtin_amdgcn_logf(den) * kLn2;
+  }
+  if (V == 4) {
+    const float4 a = *(const float4*)(o_a + off);
+    const float4 b = *(const float4*)(o_b + off);
+    float4 r;
+    if (cb == 0.f) r = ca == 0.f ? float4{0.f, 0.f, 0.f, 0.f} : a;  // exact pass-through
+    else if (ca == 0.f) r = b;
+    else r = float4{ca * a.x + cb * b.x, ca * a.y + cb * b.y, ca * a.z + cb * b.z, ca * a.w + cb * b.w};
+    *(float4*)(o_out + off) = r;
+  } else {
+    const float a = o_a[off], b = o_b[off];
+    float r;
+    if (cb == 0.f) r = ca == 0.f ? 0.f : a;
+    else if (ca == 0.f) r = b;
+    else r = ca * a + cb * b;
+    o_out[off] = r;
+  }
+  if (col == 0) lse_out[row] = lo;
+}
+
+// ---------------------------------------------------------------------------
+// Relayout ("Sequence Parallelism II: DeepSpeed Ulysses and All-to-All
+// Attention"): destination j owns heads [j Hp, (j+1) Hp), Hp = H / P_u.  Each
+// (token, destination) pair moves one contiguous run of Hp*D elements:
+//   SEQ2HEAD: in run ((b s_loc + t) P_u + j)  -> out run ((j B + b) s_loc + t)
+//   HEAD2SEQ: the reverse.
+// Threads walk the OUTPUT in order (coalesced stores); each moves one W-byte
+// unit of a run.
+template <typename W>
+__global__ __launch_bounds__(256) void relayout_kernel(int dir, uint32_t total, FastDiv upr,
+                                                       FastDiv s_loc, FastDiv pu, FastDiv bdim,
+                                                       const W* __restrict__ in, W* __restrict__ out) {
+  const uint32_t u = blockIdx.x * 256u + threadIdx.x;
+  if (u >= total) return;
+  const uint32_t run = fdiv(u, upr);
+  const uint32_t e = u - run * upr.d;
+  uint32_t src_run;
+  if (dir == 0) {
+    // out run = (j B + b) s_loc + t
+    const uint32_t jb = fdiv(run, s_loc);
+    const uint32_t t = run - jb * s_loc.d;
+    const uint32_t j = fdiv(jb, bdim);
+    const uint32_t b = jb - j * bdim.d;
+    src_run = ((b * s_loc.d) + t) * pu.d + j;
+  } else {
+    // out run = (b s_loc + t) P_u + j
+    const uint32_t bt = fdiv(run, pu);
+    const uint32_t j = run - bt * pu.d;
+    const uint32_t b = fdiv(bt, s_loc);
+    const uint32_t t = bt - b * s_loc.d;
+    src_run = (j * bdim.d + b) * s_loc.d + t;
+  }
+  out[u] = in[(long long)src_run * upr.d + e];
+}
+
+template <typename W>
+hipError_t launch_relayout_w(int dir, uint32_t total, uint32_t units_per_run, int B,
+                             long long s_loc, int P_u, const void* in, void* out, hipStream_t s) {
+  const uint32_t blocks = (total + 255u) / 256u;
+  hipLaunchKernelGGL(relayout_kernel<W>, dim3(blocks), dim3(256), 0, s, dir, total,
+                     make_fastdiv(units_per_run), make_fastdiv((uint32_t)s_loc),
+                     make_fastdiv((uint32_t)P_u), make_fastdiv((uint32_t)B), (const W*)in, (W*)out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(long long rows, int D, const float* o_a, const float* lse_a,
+                            const float* o_b, const float* lse_b, float* o_out, float* lse_out,
+                            hipStream_t s) {
+  const bool vec = (D % 4) == 0 && ((uintptr_t)o_a % 16) == 0 && ((uintptr_t)o_b % 16) == 0 &&
+                   ((uintptr_t)o_out % 16) == 0;
+  const uint32_t per_row = vec ? (uint32_t)(D / 4) : (uint32_t)D;
+  const uint32_t total = (uint32_t)(rows * per_row);
+  const uint32_t blocks = (total + 255u) / 256u;
+  if (vec)
+    hipLaunchKernelGGL(lse_merge_kernel<4>, dim3(blocks), dim3(256), 0, s, total,
+                       make_fastdiv(per_row), D, o_a, lse_a, o_b, lse_b, o_out, lse_out);
+  else
+    hipLaunchKernelGGL(lse_merge_kernel<1>, dim3(blocks), dim3(256), 0, s, total,
+                       make_fastdiv(per_row), D, o_a, lse_a, o_b, lse_b, o_out, lse_out);
+  return hipGetLastError();
+}
+
+int relayout_unit(long long run_bytes, const void* in, const void* out) {
+  const uintptr_t a = (uintptr_t)in | (uintptr_t)out;
+  for (int w = 16; w > 1; w /= 2)
+    if (run_bytes % w == 0 && a % w == 0) return w;
+  return 1;
+}
+
+hipError_t launch_relayout(int dir, int elem_bytes, int B, long long s_loc, int H, int D, int P_u,
+                           const void* in, void* out, hipStream_t s) {
+  const long long run_bytes = (long long)(H / P_u) * D * elem_bytes;
+  const long long runs = (long long)P_u * B * s_loc;
+  const int w = relayout_unit(run_bytes, in, out);
+  const uint32_t upr = (uint32_t)(run_bytes / w), total = (uint32_t)(runs * upr);
+  switch (w) {
+    case 16: return launch_relayout_w<uint4>(dir, total, upr, B, s_loc, P_u, in, out, s);
+    case 8: return launch_relayout_w<uint2>(dir, total, upr, B, s_loc, P_u, in, out, s);
+    case 4: return launch_relayout_w<uint32_t>(dir, total, upr, B, s_loc, P_u, in, out, s);
+    case 2: return launch_relayout_w<uint16_t>(dir, total, upr, B, s_loc, P_u, in, out, s);
+    default: return launch_relayout_w<uint8_t>(dir, total, upr, B, s_loc, P_u, in, out, s);
+  }
+}
+
+}  // namespace ra

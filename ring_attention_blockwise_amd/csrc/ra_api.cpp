@@ -1,0 +1,343 @@
+// C ABI of libra.so: argument checks, the host-side plan of a ring step, the
+// rank driver, and the launches.  Every check runs before anything is
+// enqueued, so a failing call leaves the caller's buffers untouched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "ra.h"
+#include "ra_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return RA_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ---------------------------------------------------------------------------
+// Index maps.  Contiguous: rank r owns [r S/P, (r+1) S/P).  Zigzag: 2P chunks
+// of c = S/(2P); rank r owns chunk r, then chunk 2P-1-r.  Ring: at step s rank
+// r holds the shard of (r - s) mod P.
+struct Spans {
+  int n;
+  ra_span s[2];
+};
+
+int check_ring(int32_t order, int64_t S, int32_t P, int32_t rank) {
+  if (order != RA_ORDER_CONTIGUOUS && order != RA_ORDER_ZIGZAG)
+    return fail(RA_E_INVAL, "order must be RA_ORDER_CONTIGUOUS or RA_ORDER_ZIGZAG (got %d)", order);
+  if (P < 1) return fail(RA_E_INVAL, "P must be >= 1 (got %d)", P);
+  if (S < 0) return fail(RA_E_INVAL, "S must be >= 0");
+  if (rank < 0 || rank >= P) return fail(RA_E_INVAL, "rank %d outside [0, %d)", rank, P);
+  const int64_t parts = order == RA_ORDER_ZIGZAG ? 2LL * P : (int64_t)P;
+  if (S % parts != 0)
+    return fail(RA_E_INVAL, "S = %lld is not divisible by %lld chunks", (long long)S, (long long)parts);
+  return RA_OK;
+}
+
+Spans rank_spans(int32_t order, int64_t S, int32_t P, int32_t rank) {
+  Spans sp;
+  if (order == RA_ORDER_CONTIGUOUS) {
+    const int64_t c = S / P;
+    sp.n = 1;
+    sp.s[0] = {rank * c, c};
+  } else {
+    const int64_t c = S / (2LL * P);
+    sp.n = 2;
+    sp.s[0] = {rank * c, c};
+    sp.s[1] = {(2LL * P - 1 - rank) * c, c};
+  }
+  return sp;
+}
+
+int32_t ring_src(int32_t rank, int32_t step, int32_t P) { return ((rank - step) % P + P) % P; }
+
+// Class of query positions [q0, q0+nq) against key positions [k0, k0+nk).
+int32_t pair_class(int64_t q0, int64_t nq, int64_t k0, int64_t nk, bool causal) {
+  if (nq <= 0 || nk <= 0) return RA_CLASS_SKIP;
+  if (!causal) return RA_CLASS_FULL;
+  if (k0 > q0 + nq - 1) return RA_CLASS_SKIP;
+  if (k0 + nk - 1 <= q0) return RA_CLASS_FULL;
+  return RA_CLASS_DIAG;
+}
+
+// ---------------------------------------------------------------------------
+int check_step(const ra_step_desc* d, const void* q, const void* k, const void* v, const float* o,
+               const float* lse, uint32_t flags) {
+  if (!d) return fail(RA_E_INVAL, "descriptor is NULL");
+  if (d->dtype != RA_DTYPE_F32 && d->dtype != RA_DTYPE_BF16)
+    return fail(RA_E_UNSUPPORTED, "dtype %d not supported (RA_DTYPE_F32 or RA_DTYPE_BF16)", d->dtype);
+  if (d->D != 64 && d->D != 128) return fail(RA_E_UNSUPPORTED, "head dimension %d not built (64 or 128)", d->D);
+  if (d->B < 1 || d->Hq < 1 || d->Hkv < 1) return fail(RA_E_INVAL, "B, Hq, Hkv must be >= 1");
+  if (d->Hq % d->Hkv) return fail(RA_E_INVAL, "Hq = %d is not a multiple of Hkv = %d", d->Hq, d->Hkv);
+  if (d->Sq < 0 || d->Sk < 0) return fail(RA_E_INVAL, "Sq and Sk must be >= 0");
+  if (flags != RA_STEP_INIT && flags != RA_STEP_ACCUM) return fail(RA_E_INVAL, "unknown flags 0x%x", flags);
+  if (!(std::isfinite(d->scale) && d->scale > 0.f)) return fail(RA_E_INVAL, "scale must be finite and > 0");
+  if (d->n_qspans < 1 || d->n_qspans > 2 || d->n_kspans < 1 || d->n_kspans > 2)
+    return fail(RA_E_INVAL, "n_qspans and n_kspans must be 1 or 2");
+  int64_t sq = 0, sk = 0;
+  for (int i = 0; i < d->n_qspans; ++i) {
+    if (d->qspans[i].len < 0 || d->qspans[i].start < 0) return fail(RA_E_INVAL, "query span %d is negative", i);
+    sq += d->qspans[i].len;
+  }
+  for (int i = 0; i < d->n_kspans; ++i) {
+    if (d->kspans[i].len < 0 || d->kspans[i].start < 0) return fail(RA_E_INVAL, "key span %d is negative", i);
+    sk += d->kspans[i].len;
+  }
+  if (sq != d->Sq) return fail(RA_E_INVAL, "query spans sum to %lld, Sq = %lld", (long long)sq, (long long)d->Sq);
+  if (sk != d->Sk) return fail(RA_E_INVAL, "key spans sum to %lld, Sk = %lld", (long long)sk, (long long)d->Sk);
+  const int64_t qtiles = (d->qspans[0].len + ra::kBQ - 1) / ra::kBQ +
+                         (d->n_qspans > 1 ? (d->qspans[1].len + ra::kBQ - 1) / ra::kBQ : 0);
+  if ((int64_t)d->B * d->Hq * qtiles > (int64_t)1 << 30) return fail(RA_E_INVAL, "too many query tiles");
+  if (d->Sq > 0) {
+    if (!q || !o || !lse) return fail(RA_E_INVAL, "q, o and lse must not be NULL");
+    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 4))
+      return fail(RA_E_INVAL, "q and o must be 16-byte aligned, lse 4-byte aligned");
+  }
+  if (d->Sq > 0 && d->Sk > 0) {
+    if (!k || !v) return fail(RA_E_INVAL, "k and v must not be NULL");
+    if (!aligned(k, 16) || !aligned(v, 16)) return fail(RA_E_INVAL, "k and v must be 16-byte aligned");
+  }
+  return RA_OK;
+}
+
+// Builds the kernel parameters of one step.  Returns false when nothing has to
+// be launched (empty rows, or ACCUM with every pair masked).
+bool build_params(const ra_step_desc* d, const void* q, const void* k, const void* v, float* o,
+                  float* lse, bool accum, ra::StepParams* p) {
+  if (d->Sq == 0) return false;
+  p->q = q;
+  p->k = k;
+  p->v = v;
+  p->o = o;
+  p->lse = lse;
+  p->B = d->B;
+  p->Hq = d->Hq;
+  p->Hkv = d->Hkv;
+  p->G = d->Hq / d->Hkv;
+  p->Sq = d->Sq;
+  p->Sk = d->Sk;
+  p->causal = d->causal ? 1 : 0;
+  p->accum = accum ? 1 : 0;
+  p->scale = d->scale;
+  p->sl2 = (float)((double)d->scale * 1.4426950408889634);
+  p->nks = 0;
+  int64_t off = 0;
+  for (int i = 0; i < d->n_kspans; ++i) {
+    if (d->kspans[i].len > 0) {
+      p->ks_start[p->nks] = d->kspans[i].start;
+      p->ks_len[p->nks] = d->kspans[i].len;
+      p->ks_off[p->nks] = off;
+      ++p->nks;
+    }
+    off += d->kspans[i].len;
+  }
+  p->nqs = 0;
+  off = 0;
+  for (int i = 0; i < d->n_qspans; ++i) {
+    const ra_span qs = d->qspans[i];
+    bool any = false;
+    for (int j = 0; j < p->nks; ++j)
+      any |= pair_class(qs.start, qs.len, p->ks_start[j], p->ks_len[j], p->causal) != RA_CLASS_SKIP;
+    if (qs.len > 0 && (any || !accum)) {
+      p->qs_start[p->nqs] = qs.start;
+      p->qs_len[p->nqs] = qs.len;
+      p->qs_off[p->nqs] = off;
+      ++p->nqs;
+    }
+    off += qs.len;
+  }
+  if (p->nqs == 0) return false;
+  for (int i = p->nqs; i < 2; ++i) p->qs_start[i] = p->qs_len[i] = p->qs_off[i] = 0;
+  for (int i = p->nks; i < 2; ++i) p->ks_start[i] = p->ks_len[i] = p->ks_off[i] = 0;
+  p->qt_span0 = (int)((p->qs_len[0] + ra::kBQ - 1) / ra::kBQ);
+  p->n_qtiles = p->qt_span0 + (int)((p->qs_len[1] + ra::kBQ - 1) / ra::kBQ);
+  p->n_work = p->B * p->Hq * p->n_qtiles;
+  p->per_xcd = (p->n_work + 7) / 8;
+  return true;
+}
+
+int launch_step(const ra::StepParams& p, int dtype, int D, void* stream) {
+  hipError_t e = ra::launch_attn_step(p, dtype, D, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RA_E_HIP, "attention step launch failed: %s", hipGetErrorString(e));
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_abi_version(void) { return RA_ABI_VERSION; }
+
+const char* ra_last_error(void) { return g_err; }
+
+int ra_plan(int32_t order, int64_t S, int32_t P, int32_t rank, int32_t step, int32_t causal, int32_t tile_q,
+            int32_t tile_k, ra_plan_out* out) {
+  if (!out) return fail(RA_E_INVAL, "out is NULL");
+  int rc = check_ring(order, S, P, rank);
+  if (rc) return rc;
+  if (step < 0 || step >= P) return fail(RA_E_INVAL, "step %d outside [0, %d)", step, P);
+  if (tile_q < 1 || tile_k < 1) return fail(RA_E_INVAL, "tile sizes must be >= 1");
+  const int32_t src = ring_src(rank, step, P);
+  const Spans qs = rank_spans(order, S, P, rank), ks = rank_spans(order, S, P, src);
+  out->src = src;
+  out->n_qspans = qs.n;
+  out->n_kspans = ks.n;
+  for (int i = 0; i < 2; ++i) {
+    out->qspans[i] = i < qs.n ? qs.s[i] : ra_span{0, 0};
+    out->kspans[i] = i < ks.n ? ks.s[i] : ra_span{0, 0};
+    for (int j = 0; j < 2; ++j)
+      out->pair_class[i][j] = (i < qs.n && j < ks.n)
+                                  ? pair_class(qs.s[i].start, qs.s[i].len, ks.s[j].start, ks.s[j].len, causal != 0)
+                                  : RA_CLASS_SKIP;
+  }
+  // Tile counts: per span pair, count tiles by class.  For a causal pair the
+  // class of (query tile [a, a+tq), key tile [b, b+tk)) only depends on the
+  // two ends, so each query tile's key tiles split into a FULL prefix, a DIAG
+  // middle and a SKIP suffix; the loop is over query tiles only.
+  int64_t nf = 0, nd = 0, ns = 0;
+  for (int i = 0; i < qs.n; ++i) {
+    for (int j = 0; j < ks.n; ++j) {
+      const int64_t qa = qs.s[i].start, qn = qs.s[i].len, ka = ks.s[j].start, kn = ks.s[j].len;
+      const int64_t nkt = (kn + tile_k - 1) / tile_k;
+      for (int64_t a = 0; a < qn; a += tile_q) {
+        const int64_t q0 = qa + a, q1 = qa + (a + tile_q < qn ? a + tile_q : qn);  // [q0, q1)
+        if (!causal) {
+          nf += nkt;
+          continue;
+        }
+        // key tile t spans [ka + t tk, min(ka + (t+1) tk, ka + kn))
+        int64_t full = 0, skip = 0;
+        for (int64_t t = 0; t < nkt; ++t) {
+          const int64_t k0 = ka + t * tile_k;
+          const int64_t k1 = ka + ((t + 1) * tile_k < kn ? (t + 1) * tile_k : kn);
+          const int32_t c = pair_class(q0, q1 - q0, k0, k1 - k0, true);
+          if (c == RA_CLASS_FULL) {
+            ++full;
+          } else if (c == RA_CLASS_SKIP) {
+            // key tiles only move right from here: the rest are SKIP too
+            skip += nkt - t;
+            break;
+          }
+        }
+        nf += full;
+        ns += skip;
+        nd += nkt - full - skip;
+      }
+    }
+  }
+  out->tiles_full = nf;
+  out->tiles_diag = nd;
+  out->tiles_skip = ns;
+  return ok();
+}
+
+int ra_step(const ra_step_desc* d, const void* q, const void* k, const void* v, float* o, float* lse,
+            uint32_t flags, void* stream) {
+  int rc = check_step(d, q, k, v, o, lse, flags);
+  if (rc) return rc;
+  ra::StepParams p;
+  if (!build_params(d, q, k, v, o, lse, flags == RA_STEP_ACCUM, &p)) return ok();
+  rc = launch_step(p, d->dtype, d->D, stream);
+  return rc ? rc : ok();
+}
+
+int ra_rank_forward(const ra_rank_desc* d, const void* q_local, const void* k_shards, const void* v_shards,
+                    float* o, float* lse, void* stream) {
+  if (!d) return fail(RA_E_INVAL, "descriptor is NULL");
+  int rc = check_ring(d->order, d->S, d->P, d->rank);
+  if (rc) return rc;
+  const int64_t s_loc = d->S / d->P;
+  const size_t esz = d->dtype == RA_DTYPE_BF16 ? 2 : 4;
+  // Validate every step's descriptor before the first launch.
+  ra_step_desc sd;
+  sd.dtype = d->dtype;
+  sd.B = d->B;
+  sd.Hq = d->Hq;
+  sd.Hkv = d->Hkv;
+  sd.D = d->D;
+  sd.Sq = s_loc;
+  sd.Sk = s_loc;
+  sd.causal = d->causal;
+  sd.scale = d->scale;
+  const Spans qs = rank_spans(d->order, d->S, d->P, d->rank);
+  sd.n_qspans = qs.n;
+  for (int i = 0; i < 2; ++i) sd.qspans[i] = i < qs.n ? qs.s[i] : ra_span{0, 0};
+  const int64_t shard_elems = (int64_t)d->B * s_loc * d->Hkv * d->D;
+  {
+    const Spans ks = rank_spans(d->order, d->S, d->P, d->rank);
+    sd.n_kspans = ks.n;
+    for (int i = 0; i < 2; ++i) sd.kspans[i] = i < ks.n ? ks.s[i] : ra_span{0, 0};
+    rc = check_step(&sd, q_local, k_shards, v_shards, o, lse, RA_STEP_INIT);
+    if (rc) return rc;
+  }
+  if (s_loc == 0) return ok();
+  for (int32_t s = 0; s < d->P; ++s) {
+    const int32_t src = ring_src(d->rank, s, d->P);
+    const Spans ks = rank_spans(d->order, d->S, d->P, src);
+    sd.n_kspans = ks.n;
+    for (int i = 0; i < 2; ++i) sd.kspans[i] = i < ks.n ? ks.s[i] : ra_span{0, 0};
+    const char* kp = (const char*)k_shards + (size_t)src * shard_elems * esz;
+    const char* vp = (const char*)v_shards + (size_t)src * shard_elems * esz;
+    ra::StepParams p;
+    if (!build_params(&sd, q_local, kp, vp, o, lse, s > 0, &p)) continue;
+    rc = launch_step(p, d->dtype, d->D, stream);
+    if (rc) return rc;
+  }
+  return ok();
+}
+
+int ra_lse_merge(int64_t rows, int32_t D, const float* o_a, const float* lse_a, const float* o_b,
+                 const float* lse_b, float* o_out, float* lse_out, void* stream) {
+  if (rows < 0) return fail(RA_E_INVAL, "rows must be >= 0");
+  if (D < 1 || D > 4096) return fail(RA_E_INVAL, "D = %d outside [1, 4096]", D);
+  if (rows == 0) return ok();
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out) return fail(RA_E_INVAL, "NULL pointer");
+  if (!aligned(o_a, 4) || !aligned(o_b, 4) || !aligned(o_out, 4) || !aligned(lse_a, 4) ||
+      !aligned(lse_b, 4) || !aligned(lse_out, 4))
+    return fail(RA_E_INVAL, "pointers must be 4-byte aligned");
+  if (rows * (int64_t)D >= ((int64_t)1 << 31)) return fail(RA_E_INVAL, "rows * D must be < 2^31");
+  hipError_t e = ra::launch_lse_merge(rows, D, o_a, lse_a, o_b, lse_b, o_out, lse_out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RA_E_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int ra_ulysses_relayout(int32_t dir, int32_t elem_bytes, int32_t B, int64_t s_loc, int32_t H, int32_t D,
+                        int32_t P_u, const void* in, void* out, void* stream) {
+  if (dir != RA_SEQ2HEAD && dir != RA_HEAD2SEQ) return fail(RA_E_INVAL, "dir must be RA_SEQ2HEAD or RA_HEAD2SEQ");
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+    return fail(RA_E_INVAL, "elem_bytes must be 1, 2, 4 or 8");
+  if (B < 0 || s_loc < 0 || H < 1 || D < 0 || P_u < 1) return fail(RA_E_INVAL, "bad shape");
+  if (H % P_u) return fail(RA_E_INVAL, "H = %d is not divisible by P_u = %d", H, P_u);
+  const int64_t bytes = (int64_t)B * s_loc * H * D * elem_bytes;
+  if (bytes == 0) return ok();
+  if (!in || !out) return fail(RA_E_INVAL, "NULL pointer");
+  const uintptr_t i0 = (uintptr_t)in, o0 = (uintptr_t)out;
+  if (i0 < o0 + (uintptr_t)bytes && o0 < i0 + (uintptr_t)bytes) return fail(RA_E_INVAL, "in and out overlap");
+  const int64_t runs = (int64_t)P_u * B * s_loc;
+  const int64_t run_bytes = (int64_t)(H / P_u) * D * elem_bytes;
+  const int64_t units = runs * (run_bytes / ra::relayout_unit(run_bytes, in, out));
+  if (runs >= ((int64_t)1 << 31) || units >= ((int64_t)1 << 31))
+    return fail(RA_E_INVAL, "tensor too large for one relayout call (2^31 copy units)");
+  hipError_t e = ra::launch_relayout(dir, elem_bytes, B, s_loc, H, D, P_u, in, out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RA_E_HIP, "relayout launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Internal interface between the C ABI (ra_api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+// Query rows per workgroup (4 waves x 32 rows) and keys per LDS tile.
+constexpr int kBQ = 128;
+constexpr int kBK = 64;
+
+// Everything one launch of the attention step kernel needs.  Spans are the
+// (at most two) query / key spans of the step in local row order; only query
+// spans that have work are listed (in ACCUM mode a span that sees no key is
+// dropped so its workgroups are never launched).
+struct StepParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  float* lse;
+  int B, Hq, Hkv, G;        // G = Hq / Hkv
+  long long Sq, Sk;         // rows of q / k (row strides of the batch dim)
+  int causal, accum;
+  float scale, sl2;         // sl2 = scale * log2(e)
+  int nqs, nks;
+  long long qs_start[2], qs_len[2], qs_off[2];
+  long long ks_start[2], ks_len[2], ks_off[2];
+  int qt_span0;             // query tiles in listed query span 0
+  int n_qtiles;             // query tiles per (batch, head)
+  int n_work;               // B * Hq * n_qtiles
+  int per_xcd;              // ceil(n_work / 8)
+};
+
+// dtype: 0 = f32, 1 = bf16; D in {64, 128}.
+hipError_t launch_attn_step(const StepParams& p, int dtype, int D, hipStream_t s);
+
+hipError_t launch_lse_merge(long long rows, int D, const float* o_a,
+                            const float* lse_a, const float* o_b,
+                            const float* lse_b, float* o_out, float* lse_out,
+                            hipStream_t s);
+
+// Bytes moved per thread by the relayout kernel for these runs and pointers.
+int relayout_unit(long long run_bytes, const void* in, const void* out);
+
+hipError_t launch_relayout(int dir, int elem_bytes, int B, long long s_loc,
+                           int H, int D, int P_u, const void* in, void* out,
+                           hipStream_t s);
+
+}  // namespace ra

@@ -1,0 +1,71 @@
+"""The library's host plan (ra_plan) against the oracle's index maps, bit-exact.
+CPU only: ra_plan does integer work on the host and touches no GPU."""
+import numpy as np
+import pytest
+
+from oracle import index_maps as im
+from seeded_inputs import WORKLOADS
+
+ra = pytest.importorskip("ring_attention_blockwise_amd")
+
+KERNEL_TILES = (128, 64)
+
+
+def _check(order, S, P, r, s, causal, tq, tk, with_tiles=True):
+    got = ra.ra_plan(order, S, P, r, s, causal, tq, tk)
+    src = im.ring_source(r, s, P)
+    assert got["src"] == src
+    assert got["qspans"] == im.rank_spans(S, P, r, order)
+    assert got["kspans"] == im.rank_spans(S, P, src, order)
+    classes = [[im.block_class(a, a + n, b, b + m, causal) for (b, m) in got["kspans"]]
+               for (a, n) in got["qspans"]]
+    assert got["classes"] == classes
+    assert got["classes"] == im.step_pair_classes(S, P, r, s, order, causal)
+    if with_tiles:
+        assert got["tiles"] == im.tile_counts(S, P, r, s, order, causal, tq, tk)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_plan_matches_oracle_on_workloads(name):
+    w = WORKLOADS[name]
+    ranks = range(w.P) if w.P <= 16 else (0, 1, w.P // 2, w.P - 2, w.P - 1)
+    for r in ranks:
+        for s in range(w.P):
+            _check(w.order, w.S, w.P, r, s, w.causal, *KERNEL_TILES,
+                   with_tiles=(w.S <= 131072 or s % 8 == 0))
+
+
+@pytest.mark.parametrize("order", ["contiguous", "zigzag"])
+def test_plan_matches_oracle_random_small(order):
+    rng = np.random.default_rng(11)
+    for _ in range(150):
+        P = int(rng.integers(1, 9))
+        c = int(rng.integers(1, 40))
+        S = c * (2 * P if order == "zigzag" else P)
+        r, s = int(rng.integers(0, P)), int(rng.integers(0, P))
+        tq, tk = int(rng.integers(1, 50)), int(rng.integers(1, 50))
+        _check(order, S, P, r, s, bool(rng.integers(0, 2)), tq, tk)
+
+
+def test_rank_spans_are_the_oracle_map():
+    for order in ("contiguous", "zigzag"):
+        for S, P in ((64, 4), (131072, 16), (524288, 32)):
+            for r in range(P):
+                spans = ra.rank_spans(order, S, P, r)
+                pos = np.concatenate([np.arange(a, a + n) for a, n in spans])
+                np.testing.assert_array_equal(pos, im.rank_positions(S, P, r, order))
+
+
+@pytest.mark.parametrize("args", [
+    ("zigzag", 100, 8, 0, 0),      # S not divisible by 2P
+    ("contiguous", 10, 4, 0, 0),   # S not divisible by P
+    ("zigzag", 64, 4, 4, 0),       # rank out of range
+    ("zigzag", 64, 4, 0, 4),       # step out of range
+    ("zigzag", 64, 0, 0, 0),       # P < 1
+])
+def test_plan_rejects_bad_rings(args):
+    order, S, P, r, s = args
+    with pytest.raises(ra.RaError) as e:
+        ra.ra_plan(order, S, P, r, s, True, 64, 64)
+    assert e.value.status == ra.RA_E_INVAL
+    assert ra.ra_last_error()
