@@ -1,0 +1,310 @@
+"""Throughput of one rank's blockwise ring attention on one MI355X.
+
+A step is one ra_rank_forward call: rank 0 of a 131,072-token causal zigzag
+ring of 16 ranks (bf16, batch 1, 32 query heads over 8 K/V heads, head dim 128,
+8,192 local query rows), all 16 ring steps with their fused log-sum-exp merges.
+Inputs are seeded synthetic tensors already resident in HBM.  The value is
+algorithmic TFLOP/s: 4*D FLOPs per visible (query, key) pair per head, divided
+by the measured time (pairs hidden by the causal mask are not counted).
+
+Also reported:
+  roofline      the attention step kernel against the bf16 dense MFMA peak,
+                average launch duration from HIP events on the launch stream;
+  cpu_baseline  the CPU oracle (float64 numpy) timed on a sample of rows;
+  aux           HBM rates of the standalone merge and of the relayout.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "attention TFLOPS per rank-share (1 GPU) and % of bf16 MFMA peak"
+KERNEL_SOURCES = ["ring_attention_blockwise_amd/csrc/attn_step.hip",
+                  "ring_attention_blockwise_amd/csrc/ra_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_step_traffic.json")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source for this workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash() or t.get("workload") != workload_name:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def to_device(x, dtype):
+    import torch
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def build_inputs(ra, w, rank):
+    import torch
+    import seeded_inputs as si
+    s_loc = w.S // w.P
+    q = to_device(si.tokens(w.seed_id, si.TENSOR_Q, w.B, w.S, w.Hq, w.D,
+                            ra.rank_spans(w.order, w.S, w.P, rank), w.dtype), w.dtype)
+    shards = []
+    for tid, scale in ((si.TENSOR_K, w.k_scale), (si.TENSOR_V, 1.0)):
+        out = torch.empty((w.P, w.B, s_loc, w.Hkv, w.D), dtype=q.dtype, device="cuda")
+        for p in range(w.P):
+            out[p] = to_device(si.tokens(w.seed_id, tid, w.B, w.S, w.Hkv, w.D,
+                                         ra.rank_spans(w.order, w.S, w.P, p), w.dtype, scale=scale),
+                               w.dtype)
+        shards.append(out)
+    o = torch.empty((w.B, s_loc, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, s_loc, w.Hq), dtype=torch.float32, device="cuda")
+    return q, shards[0], shards[1], o, lse
+
+
+def launches_per_step(ra, w, rank):
+    """Steps of the ring that launch the kernel (a step whose whole block is
+    masked is skipped by ra_rank_forward)."""
+    n = 0
+    for s in range(w.P):
+        plan = ra.ra_plan(w.order, w.S, w.P, rank, s, w.causal, 1 << 30, 1 << 30)
+        if s == 0 or any(c != "SKIP" for row in plan["classes"] for c in row):
+            n += 1
+    return n
+
+
+def algorithmic_flops(w, rank):
+    """4*D per visible pair per (batch, head), pairs from the closed forms of
+    the chunk maps (zigzag: c(S+1) per rank; contiguous: s^2 r + s(s+1)/2)."""
+    s_loc = w.S // w.P
+    if not w.causal:
+        pairs = s_loc * w.S
+    elif w.order == "zigzag":
+        c = w.S // (2 * w.P)
+        pairs = c * (w.S + 1)
+    else:
+        pairs = s_loc * s_loc * rank + s_loc * (s_loc + 1) // 2
+    return 4.0 * w.D * w.B * w.Hq * pairs
+
+
+def time_attention(ra, w, rank, steps, warmup):
+    import torch
+    q, ks, vs, o, lse = build_inputs(ra, w, rank)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ra.ra_rank_forward(q, ks, vs, o, lse, S=w.S, P=w.P, rank=rank, order=w.order,
+                           causal=w.causal, scale=w.scale, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]   # ms, HIP events on the launch stream
+    ok = bool(torch.isfinite(o).all().item() and torch.isfinite(lse).all().item())
+    del q, ks, vs, o, lse
+    torch.cuda.empty_cache()
+    return wall, per, ok
+
+
+def time_merge(ra, rows, D, reps=20):
+    """Standalone merge, rotating buffer sets so the working set exceeds the
+    256 MB Infinity Cache."""
+    import torch
+    per_call = rows * (12 * D + 12)
+    nsets = max(2, int(np.ceil(1.2e9 / per_call)))
+    sets = []
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for _ in range(nsets):
+        sets.append(tuple(torch.randn(rows, D, device="cuda", generator=g) for _ in range(3)) +
+                    tuple(torch.randn(rows, device="cuda", generator=g) for _ in range(3)))
+    for s in sets:
+        ra.ra_lse_merge(s[0], s[3], s[1], s[4], s[2], s[5])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        s = sets[i % nsets]
+        ra.ra_lse_merge(s[0], s[3], s[1], s[4], s[2], s[5])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del sets
+    torch.cuda.empty_cache()
+    return {"kernel": "lse_merge", "rows": rows, "D": D, "bytes": per_call, "us": ms * 1e3,
+            "GB/s": per_call / (ms * 1e-3) / 1e9, "frac_hbm": per_call / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+def time_relayout(ra, B, s_loc, H, D, P_u, reps=20):
+    import torch
+    nbytes = B * s_loc * H * D * 2
+    nsets = max(2, int(np.ceil(1.2e9 / (2 * nbytes))))
+    xs = [torch.randn(B, s_loc, H, D, device="cuda").to(torch.bfloat16) for _ in range(nsets)]
+    ys = [torch.empty(P_u, B, s_loc, H // P_u, D, device="cuda", dtype=torch.bfloat16) for _ in range(nsets)]
+    for x, y in zip(xs, ys):
+        ra.ra_ulysses_relayout(x, y, P_u, ra.RA_SEQ2HEAD)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        ra.ra_ulysses_relayout(xs[i % nsets], ys[i % nsets], P_u, ra.RA_SEQ2HEAD)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    moved = 2 * nbytes
+    del xs, ys
+    torch.cuda.empty_cache()
+    return {"kernel": "ulysses_relayout_seq2head", "shape": [B, s_loc, H, D], "P_u": P_u, "bytes": moved,
+            "us": ms * 1e3, "GB/s": moved / (ms * 1e-3) / 1e9,
+            "frac_hbm": moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+def cpu_baseline(w, rank, target_s=15.0):
+    """The CPU oracle, as it stands, on a bounded sample of rank ``rank``'s rows
+    (all heads), scaled to TFLOP/s by the algorithmic FLOPs of those rows."""
+    import seeded_inputs as si
+    from oracle import attention as oa
+    from oracle import index_maps as im
+    pos = im.rank_positions(w.S, w.P, rank, w.order)
+    rng = np.random.default_rng(1234)
+    Kg = si.tokens(w.seed_id, si.TENSOR_K, w.B, w.S, w.Hkv, w.D, [(0, w.S)], w.dtype, scale=w.k_scale)
+    Vg = si.tokens(w.seed_id, si.TENSOR_V, w.B, w.S, w.Hkv, w.D, [(0, w.S)], w.dtype)
+    Kf, Vf = si.to_f64(Kg, w.dtype), si.to_f64(Vg, w.dtype)
+    del Kg, Vg
+    done_flops, done_s, rows_done = 0.0, 0.0, 0
+    while done_s < target_s and rows_done < pos.size:
+        rows = np.sort(rng.choice(pos.size, 16, replace=False))
+        qsel = pos[rows]
+        q = si.to_f64(si.tokens(w.seed_id, si.TENSOR_Q, w.B, w.S, w.Hq, w.D,
+                                [(int(t), 1) for t in qsel], w.dtype), w.dtype)
+        t0 = time.perf_counter()
+        oa.attention_rows(q, qsel, Kf, Vf, np.arange(w.S), w.causal, w.scale)
+        done_s += time.perf_counter() - t0
+        vis = (qsel + 1).sum() if w.causal else qsel.size * w.S
+        done_flops += 4.0 * w.D * w.B * w.Hq * float(vis)
+        rows_done += rows.size
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": done_flops / done_s / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows_done} random query rows of rank {rank} x {w.Hq} heads x all visible keys, "
+                      f"float64 numpy, {done_s:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None, help="workload name (default: the 131k zigzag ring)")
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-aux", action="store_true", help="skip merge/relayout rates")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 1 GiB device copy (scale reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one rank's ring steps on one GPU; --gpus {args.gpus} is not "
+              "supported (the ring's other ranks are simulated on this GPU, and no collective "
+              "between GPUs is part of this library).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calib:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_read": 1 << 30, "copy_calib_bytes_written": 1 << 30, "copies": 3}))
+        return
+    import ring_attention_blockwise_amd as ra
+    from seeded_inputs import workload
+    from seeded_inputs.workloads import HEADLINE
+
+    name = args.workload or HEADLINE
+    w = workload(name)
+    rank = args.rank
+    print(f"[bench] {name} rank {rank}: generating inputs", file=sys.stderr, flush=True)
+    wall, per, ok = time_attention(ra, w, rank, args.steps, args.warmup)
+    flops = algorithmic_flops(w, rank)
+    ms = float(np.mean(per))
+    value = flops / (ms * 1e-3) / 1e12
+    nl = launches_per_step(ra, w, rank)
+    launch_us = ms * 1e3 / nl
+    achieved = flops / nl / (launch_us * 1e-6) / 1e12
+    print(f"[bench] attention: {ms:.3f} ms/step (min {min(per):.3f}), {value:.1f} TFLOP/s, "
+          f"{nl} launches of {launch_us:.1f} us", file=sys.stderr, flush=True)
+    aux = []
+    if not args.no_aux:
+        aux.append(time_merge(ra, w.B * (w.S // w.P) * w.Hq, w.D))
+        aux.append(time_relayout(ra, 2, 8192, 16, 128, 8))
+        for a in aux:
+            print(f"[bench] {a['kernel']}: {a['us']:.1f} us, {a['GB/s']:.0f} GB/s", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, rank)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) bf16, resident in HBM)",
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "S": w.S,
+                   "ring": w.P, "rank": rank, "order": w.order, "causal": w.causal,
+                   "local_query_rows": w.S // w.P},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(name), "kernel": "attn_step_kernel<Bf16<128>>",
+                     "launches_per_step": nl, "avg_launch_us": round(launch_us, 2)},
+        "cpu_baseline": cpu,
+        "aux": aux,
+        "outputs_finite": ok,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
