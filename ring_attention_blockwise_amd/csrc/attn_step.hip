@@ -10,19 +10,23 @@
 // (O, LSE) held in HBM.
 //
 // Work decomposition
-//   * A workgroup (4 waves) owns 128 consecutive query rows of one (batch,
-//     query head); wave w owns rows [32w, 32w + 32).
-//   * Keys are processed in tiles of 64, staged in LDS and double buffered:
-//     tile t+1 is fetched into registers while tile t is computed, then stored
-//     to the other LDS buffer.
-//   * Only key tiles with at least one visible key are visited.  A tile that
-//     straddles the causal diagonal, or is cut short by the end of a span, runs
-//     the mask code; every other tile runs none.
+//   * A workgroup (4 waves, one per SIMD) owns 128 consecutive query rows of
+//     one (batch, query head); wave w owns rows [32w, 32w + 32).  Two
+//     workgroups share a CU, so each SIMD interleaves two waves: while one
+//     runs its softmax on the vector ALUs, the other can issue MFMAs.
+//   * Keys are processed in tiles of 32.  Tile t+1 is loaded into registers
+//     at the start of iteration t and written to the other LDS buffer (two
+//     each for K and V) at its end; the loop is unrolled by two so that every
+//     LDS buffer is named statically.
+//   * Only key tiles with at least one visible key are visited.  Tiles whose
+//     keys every query row of the work item sees run first with no mask code;
+//     tiles on the causal diagonal or cut short by the end of a span run last,
+//     masked.
 //   * Workgroups are ordered so that all query tiles reading the same K/V head
 //     land on the same XCD (dispatch is round-robin over the 8 XCDs), which
 //     keeps that head's K/V in one L2.
 //
-// Per-wave math (32 queries x 64 keys per tile)
+// Per-wave math (32 queries x 32 keys per tile)
 //   S^T = K Q^T on MFMA 32x32 tiles: the accumulator of a 32x32 block puts one
 //   query per lane (lane n and n+32 share query n) and 16 of its keys in that
 //   lane's registers, so the row max and row sum of the online softmax are
@@ -49,23 +53,23 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;              // 4 waves
+constexpr int kQB = kBQ / 128;              // 32-row query blocks per wave
+constexpr int kKB = kBK / 32;               // 32-key blocks per key tile
+constexpr int kWavesPerSimd = kQB == 1 ? 2 : 1;  // register budget 256 or 512
+static_assert(kBQ == 4 * 32 * kQB, "workgroup rows");
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Grow the reference maximum only when probabilities would exceed 2^kTau.
 constexpr float kTau = 8.0f;
 
-__device__ inline float swap_halves(float x) {
+__device__ inline float max_halves(float x) {
   // v_permlane32_swap with both operands x: every lane sees x of lane ^ 32 in
   // one of the two results; max/sum of both is symmetric.
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]) - x;
-}
-
-__device__ inline float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
@@ -78,14 +82,11 @@ __device__ inline float sum_halves(float x) {
 __device__ inline u32x4 lds_load16(const RA_LDS char* base, unsigned off) {
   return *(const RA_LDS u32x4*)(base + off);
 }
-__device__ inline void lds_store16(RA_LDS char* base, unsigned off, u32x4 v) {
-  *(RA_LDS u32x4*)(base + off) = v;
-}
 
 // ---------------------------------------------------------------------------
-// LDS tile layout: 64 key rows of D elements, row-major, 16-byte chunks.  The
+// LDS tile layout: 32 key rows of D elements, row-major, 16-byte chunks.  The
 // chunk index is XOR-swizzled per row so that both the MFMA operand reads and
-// the tile stores hit distinct banks:
+// the tile fills hit distinct banks:
 //   K: chunk ^ (row mod chunks)      -- 32 rows, one chunk per lane
 //   V: chunk ^ (4 (row mod 4))       -- transposing reads, 4 rows x 4 chunks
 template <int CPR>
@@ -103,68 +104,57 @@ struct Bf16 {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kCPR = kRowBytes / 16;  // 16-byte chunks per row
   typedef uint16_t Elem;
-  struct QFrag { bf16x8 f[D / 16]; };
+  struct QFrag { bf16x8 f[kQB][D / 16]; };
 
-  // Q^T operand: lane l holds Q[query l%32][16 dc + 8 (l/32) .. +7].
-  __device__ static void load_q(QFrag& q, const Elem* row, bool ok, int lane) {
+  // Q^T operand of block qb: lane l holds Q[query l%32][16 dc + 8 (l/32) .. +7].
+  __device__ static void load_q(QFrag& q, int qb, const Elem* row, bool ok, int lane) {
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-      if (ok) {
-        q.f[dc] = *(const bf16x8*)(row + 16 * dc + 8 * (lane >> 5));
-      } else {
-        q.f[dc] = bf16x8{};
-      }
-    }
+    for (int dc = 0; dc < D / 16; ++dc)
+      q.f[qb][dc] = ok ? *(const bf16x8*)(row + 16 * dc + 8 * (lane >> 5)) : bf16x8{};
   }
 
-  // S^T block kb (keys 32kb..32kb+31 of the tile) = K Q^T.
-  __device__ static f32x16 s_block(const RA_LDS char* kt, int kb, const QFrag& q, int lane) {
-    f32x16 acc = {};
+  // One K operand read of S^T block kb (keys 32kb..32kb+31 of the tile),
+  // reduction over d in [16u, 16u+16), feeding the MFMA of every query block.
+  static constexpr int kSUnits = D / 16;
+  __device__ static void s_unit(f32x16* acc, const RA_LDS char* kt, int kb, int u, const QFrag& q, int lane) {
     const unsigned row = 32 * kb + (lane & 31);
+    const unsigned c = 2 * u + (lane >> 5);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(kt, row * kRowBytes + ((c ^ swz_k<kCPR>(row)) * 16)));
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-      const unsigned c = 2 * dc + (lane >> 5);
-      u32x4 a = lds_load16(kt, row * kRowBytes + ((c ^ swz_k<kCPR>(row)) * 16));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), q.f[dc], acc, 0, 0, 0);
-    }
-    return acc;
+    for (int qb = 0; qb < kQB; ++qb)
+      acc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.f[qb][u], acc[qb], 0, 0, 0);
   }
 
-  // O^T[db] += V^T P^T for the 64 keys of the tile.  MFMA (kb, hf) consumes
-  // accumulator registers 8hf..8hf+7 of S^T block kb, i.e. reduction index
+  // O^T[db][qb] += V^T P^T over the 16 keys 32kb + 16hf + [0, 16) of the
+  // tile.  The MFMA consumes accumulator registers 8hf..8hf+7 of S^T block kb
+  // (already exponentiated, rounded to bf16 here), i.e. reduction index
   // 8(l/32)+e <-> key 32kb + 16hf + 8(e/4) + 4(l/32) + e%4; the V^T operand is
-  // gathered with two transposing reads of 4 keys x 16 columns per lane group.
-  __device__ static void pv(f32x16* o, const RA_LDS char* vt, const f32x16* p, int lane) {
-    bf16x8 pb[2][2];
+  // gathered with two transposing reads of 4 keys x 16 columns per 16-lane
+  // group and feeds both query blocks.
+  __device__ static void pv_group(f32x16 (*o)[kQB], const RA_LDS char* vt, const f32x16 (*p)[kQB], int kb,
+                                  int hf, int lane) {
+    bf16x8 pb[kQB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int qb = 0; qb < kQB; ++qb) {
+      f32x8 x;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        f32x8 x;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = p[kb][8 * hf + e];
-        pb[kb][hf] = __builtin_convertvector(x, bf16x8);
-      }
+      for (int e = 0; e < 8; ++e) x[e] = p[kb][qb][8 * hf + e];
+      pb[qb] = __builtin_convertvector(x, bf16x8);
     }
     const int gi = lane >> 4, s = lane & 15;
+    const unsigned r1 = 32 * kb + 16 * hf + 4 * (gi >> 1) + (s >> 2);
+    const unsigned r2 = r1 + 8;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const unsigned d = 32 * db + 16 * (gi & 1) + 4 * (s & 3);
+      const unsigned o1 = r1 * kRowBytes + (((d >> 3) ^ swz_v<kCPR>(r1)) * 16) + (d & 7) * 2;
+      const unsigned o2 = r2 * kRowBytes + (((d >> 3) ^ swz_v<kCPR>(r2)) * 16) + (d & 7) * 2;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vt + o1));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vt + o2));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const unsigned r1 = 32 * kb + 16 * hf + 4 * (gi >> 1) + (s >> 2);
-          const unsigned r2 = r1 + 8;
-          const unsigned o1 = r1 * kRowBytes + (((d >> 3) ^ swz_v<kCPR>(r1)) * 16) + (d & 7) * 2;
-          const unsigned o2 = r2 * kRowBytes + (((d >> 3) ^ swz_v<kCPR>(r2)) * 16) + (d & 7) * 2;
-          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vt + o1));
-          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vt + o2));
-          typedef __attribute__((ext_vector_type(8))) short i16x8;
-          i16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[kb][hf], o[db], 0, 0, 0);
-        }
-      }
+      for (int qb = 0; qb < kQB; ++qb)
+        o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb], o[db][qb], 0, 0, 0);
     }
   }
 };
@@ -175,109 +165,295 @@ struct F32 {
   static constexpr int kRowBytes = D * 4;
   static constexpr int kCPR = kRowBytes / 16;
   typedef float Elem;
-  struct QFrag { float f[D / 2]; };
+  struct QFrag { float f[kQB][D / 2]; };
 
-  // Q^T operand of the 32x32x2 f32 MFMA: lane l holds Q[query l%32][2kk + l/32].
-  __device__ static void load_q(QFrag& q, const Elem* row, bool ok, int lane) {
+  // Q^T operand of the 32x32x2 f32 MFMA: lane l holds Q[query l%32][2u + l/32].
+  __device__ static void load_q(QFrag& q, int qb, const Elem* row, bool ok, int lane) {
 #pragma unroll
-    for (int kk = 0; kk < D / 2; ++kk) q.f[kk] = ok ? row[2 * kk + (lane >> 5)] : 0.f;
+    for (int u = 0; u < D / 2; ++u) q.f[qb][u] = ok ? row[2 * u + (lane >> 5)] : 0.f;
   }
 
   __device__ static float lds_f(const RA_LDS char* t, unsigned row, unsigned d, unsigned swz) {
     return *(const RA_LDS float*)(t + row * kRowBytes + (((d >> 2) ^ swz) * 16) + (d & 3) * 4);
   }
 
-  __device__ static f32x16 s_block(const RA_LDS char* kt, int kb, const QFrag& q, int lane) {
-    f32x16 acc = {};
+  // One K operand of S^T block kb: reduction over d in {2u, 2u+1}.
+  static constexpr int kSUnits = D / 2;
+  __device__ static void s_unit(f32x16* acc, const RA_LDS char* kt, int kb, int u, const QFrag& q, int lane) {
     const unsigned row = 32 * kb + (lane & 31);
-    const unsigned sw = swz_k<kCPR>(row);
+    const float a = lds_f(kt, row, 2 * u + (lane >> 5), swz_k<kCPR>(row));
 #pragma unroll
-    for (int kk = 0; kk < D / 2; ++kk) {
-      float a = lds_f(kt, row, 2 * kk + (lane >> 5), sw);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, q.f[kk], acc, 0, 0, 0);
-    }
-    return acc;
+    for (int qb = 0; qb < kQB; ++qb) acc[qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, q.f[qb][u], acc[qb], 0, 0, 0);
   }
 
   // MFMA (kb, j) pairs reduction index l/32 with key 32kb + 8(j/4) + 4(l/32) + j%4,
-  // which is the key accumulator register j of lane l holds.
-  __device__ static void pv(f32x16* o, const RA_LDS char* vt, const f32x16* p, int lane) {
+  // which is the key accumulator register j of lane l holds; group hf covers
+  // registers 8hf..8hf+7.
+  __device__ static void pv_group(f32x16 (*o)[kQB], const RA_LDS char* vt, const f32x16 (*p)[kQB], int kb,
+                                  int hf, int lane) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const unsigned d = 32 * db + (lane & 31);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int j = 8 * hf; j < 8 * hf + 8; ++j) {
+        const unsigned row = 32 * kb + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+        const float a = lds_f(vt, row, d, swz_v<kCPR>(row));
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const unsigned row = 32 * kb + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-          float a = lds_f(vt, row, d, swz_v<kCPR>(row));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[kb][j], o[db], 0, 0, 0);
-        }
+        for (int qb = 0; qb < kQB; ++qb)
+          o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[kb][qb][j], o[db][qb], 0, 0, 0);
       }
     }
   }
 };
 
-// Key tile t of the step: which span, where it starts, how many rows are real.
+// ---------------------------------------------------------------------------
+// Key tiles of one work item.  Tiles restart at each key span.  Within a span
+// the tiles whose keys are all visible to every query row of the work item
+// come first and run no mask code; the rest (on the causal diagonal, or cut
+// short by the span's end) follow and are masked.  The order of the tiles does
+// not change the result.
 struct KTile {
   long long local0;  // first local key row
   long long glob0;   // its global position
-  int count;         // rows of the tile that exist and may be visible
+  int count;         // rows that exist and may be visible (<= kBK)
+  bool masked;
 };
 
-__device__ inline KTile key_tile(const StepParams& p, const int* nt, const long long* khi, int t) {
-  const int s = t < nt[0] ? 0 : 1;
-  const long long kin = (long long)(t - (s ? nt[0] : 0)) * kBK;
-  KTile kt;
-  kt.local0 = p.ks_off[s] + kin;
-  kt.glob0 = p.ks_start[s] + kin;
-  kt.count = (int)min((long long)kBK, khi[s] - kin);
-  return kt;
+struct TilePlan {
+  int nf[2], nr[2];  // full and masked tiles per span
+  long long hi[2];   // keys of the span visible to the work item's last row
+  int n_full, n;
+
+  __device__ KTile tile(const StepParams& p, int t) const {
+    int s;
+    long long kin;
+    bool masked;
+    if (t < n_full) {
+      masked = false;
+      s = t < nf[0] ? 0 : 1;
+      kin = (long long)(s ? t - nf[0] : t) * kBK;
+    } else {
+      masked = true;
+      const int u = t - n_full;
+      s = u < nr[0] ? 0 : 1;
+      kin = (long long)(nf[s] + (s ? u - nr[0] : u)) * kBK;
+    }
+    KTile kt;
+    kt.local0 = p.ks_off[s] + kin;
+    kt.glob0 = p.ks_start[s] + kin;
+    kt.count = (int)min((long long)kBK, hi[s] - kin);
+    kt.masked = masked;
+    return kt;
+  }
+};
+
+__device__ inline TilePlan plan_tiles(const StepParams& p, long long qglob0, long long qglob_last) {
+  TilePlan tp;
+  tp.n_full = 0;
+  tp.n = 0;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    long long hi = 0, full = 0;
+    if (s < p.nks) {
+      hi = p.ks_len[s];
+      full = hi;
+      if (p.causal) {
+        hi = min(hi, qglob_last + 1 - p.ks_start[s]);   // keys <= the last row
+        full = min(hi, qglob0 + 1 - p.ks_start[s]);     // keys <= the first row
+      }
+      hi = max(hi, 0LL);
+      full = max(full, 0LL);
+    }
+    tp.hi[s] = hi;
+    tp.nf[s] = (int)(full / kBK);
+    tp.nr[s] = (int)((hi - (long long)tp.nf[s] * kBK + kBK - 1) / kBK);
+    tp.n_full += tp.nf[s];
+    tp.n += tp.nf[s] + tp.nr[s];
+  }
+  return tp;
 }
 
-// Staging of one K/V tile through registers: each thread moves kPer 16-byte
-// chunks of K and of V.  Rows past `count` are zero-filled.
+// ---------------------------------------------------------------------------
+// Staging of K and V tiles through registers: each thread loads kPer 16-byte
+// chunks of the K tile and of the V tile with ordinary global loads, and
+// writes them to LDS (swizzled) after the tile being finished has been
+// computed.  Routing the data through registers (rather than the LDS DMA path)
+// lets the compiler see that the MFMA operand reads of one buffer do not depend
+// on loads in flight for the other.  Rows past `count` (only in a span's last
+// tile) repeat the last real row: their keys are masked to -inf (K) and
+// weighted by exactly 0 (V).
 template <class Tr>
-struct Stage {
-  static constexpr int kChunks = kBK * Tr::kCPR;
-  static constexpr int kPer = kChunks / kThreads;
-  u32x4 kreg[kPer], vreg[kPer];
+struct TileStage {
+  static constexpr int kPer = kBK * Tr::kCPR / kThreads;
+  u32x4 k[kPer], v[kPer];
+  unsigned goff[kPer];             // global byte offset of each chunk in a full tile
+  unsigned koff[kPer], voff[kPer];  // its swizzled LDS byte offset
+  unsigned row_bytes;              // global stride between key rows
 
-  __device__ void load(const StepParams& p, int b, int g, const KTile& kt) {
-    const typename Tr::Elem* kb = (const typename Tr::Elem*)p.k;
-    const typename Tr::Elem* vb = (const typename Tr::Elem*)p.v;
+  __device__ void init(const StepParams& p) {
+    row_bytes = (unsigned)(p.Hkv * Tr::D * (int)sizeof(typename Tr::Elem));
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int idx = threadIdx.x + i * kThreads;
-      const int row = idx / Tr::kCPR, c = idx % Tr::kCPR;
-      if (row < kt.count) {
-        const long long off = (((long long)b * p.Sk + kt.local0 + row) * p.Hkv + g) * Tr::D;
-        kreg[i] = *(const u32x4*)((const char*)(kb + off) + c * 16);
-        vreg[i] = *(const u32x4*)((const char*)(vb + off) + c * 16);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
+      const unsigned idx = threadIdx.x + i * kThreads;
+      const unsigned row = idx / Tr::kCPR, c = idx % Tr::kCPR;
+      goff[i] = row * row_bytes + c * 16;
+      koff[i] = row * Tr::kRowBytes + ((c ^ swz_k<Tr::kCPR>(row)) * 16);
+      voff[i] = row * Tr::kRowBytes + ((c ^ swz_v<Tr::kCPR>(row)) * 16);
+    }
+  }
+
+  // Loads tile kt of K (is_v false) or V into the staging registers.
+  __device__ void load(const StepParams& p, int b, int g, const KTile& kt, bool is_v) {
+    const long long base = (((long long)b * p.Sk + kt.local0) * p.Hkv + g) * (long long)(Tr::D * sizeof(typename Tr::Elem));
+    const char* src = (const char*)(is_v ? p.v : p.k) + base;
+    u32x4* dst = is_v ? v : k;
+    if (kt.count == kBK) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) dst[i] = *(const u32x4*)(src + goff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const unsigned idx = threadIdx.x + i * kThreads;
+        const unsigned row = idx / Tr::kCPR, c = idx % Tr::kCPR;
+        dst[i] = *(const u32x4*)(src + min((int)row, kt.count - 1) * row_bytes + c * 16);
       }
     }
   }
 
-  __device__ void store(RA_LDS char* kt, RA_LDS char* vt) const {
+  __device__ void store_k(RA_LDS char* dst) const {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = threadIdx.x + i * kThreads;
-      const unsigned row = idx / Tr::kCPR, c = idx % Tr::kCPR;
-      lds_store16(kt, row * Tr::kRowBytes + ((c ^ swz_k<Tr::kCPR>(row)) * 16), kreg[i]);
-      lds_store16(vt, row * Tr::kRowBytes + ((c ^ swz_v<Tr::kCPR>(row)) * 16), vreg[i]);
-    }
+    for (int i = 0; i < kPer; ++i) *(RA_LDS u32x4*)(dst + koff[i]) = k[i];
+  }
+  __device__ void store_v(RA_LDS char* dst) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) *(RA_LDS u32x4*)(dst + voff[i]) = v[i];
   }
 };
 
+// Per-wave state carried across key tiles.
 template <class Tr>
-__global__ __launch_bounds__(256) void attn_step_kernel(StepParams p) {
+struct WaveState {
+  typename Tr::QFrag qf;
+  f32x16 o[Tr::D / 32][kQB];  // O^T accumulators
+  f32x16 s[kKB][kQB];         // S^T of the tile being finished
+  float m_ref[kQB];           // reference maximum of the raw (unscaled) scores
+  float l_part[kQB];          // this lane's share of the row sum
+};
+
+// Mask (masked tiles only), running maximum and, when it grows by more than
+// 2^kTau, rescale of O and l.  Leaves in mb the exp2 offset of each block.
+template <class Tr, bool kMasked>
+__device__ inline void softmax_prep(WaveState<Tr>& ws, const StepParams& p, const KTile& ti, const long long* qg,
+                                    int lane, float* mb) {
+  constexpr int D = Tr::D;
+  if (kMasked) {
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const bool vis = key < ti.count && (!p.causal || ti.glob0 + key <= qg[qb]);
+          if (!vis) ws.s[kb][qb][r] = kNegInf;
+        }
+  }
+  bool grow[kQB];
+  bool any = false;
+  float m_new[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    float tmax = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, ws.s[kb][qb][r]);
+    tmax = max_halves(tmax);
+    m_new[qb] = fmaxf(ws.m_ref[qb], tmax);
+    // -inf reference: the difference is +inf and the maximum is taken;
+    // both -inf: NaN compares false and nothing moves.
+    grow[qb] = (m_new[qb] - ws.m_ref[qb]) * p.sl2 > kTau;
+    any |= grow[qb];
+  }
+  if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float alpha = grow[qb] ? __builtin_amdgcn_exp2f((ws.m_ref[qb] - m_new[qb]) * p.sl2) : 1.f;
+      if (grow[qb]) ws.m_ref[qb] = m_new[qb];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) ws.o[db][qb] *= alpha;
+      ws.l_part[qb] *= alpha;
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) mb[qb] = ws.m_ref[qb] == kNegInf ? 0.f : ws.m_ref[qb] * p.sl2;
+}
+
+// Exponentials and O += V P for 16-key group grp of the tile in ws.s.
+template <class Tr>
+__device__ inline void softmax_pv_group(WaveState<Tr>& ws, const StepParams& p, int grp, const float* mb,
+                                        float* lsum, const RA_LDS char* vt, int lane) {
+  const int kb = grp >> 1, hf = grp & 1;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(ws.s[kb][qb][8 * hf + e], p.sl2, -mb[qb]));
+      ws.s[kb][qb][8 * hf + e] = pr;
+      lsum[qb] += pr;
+    }
+  Tr::pv_group(ws.o, vt, ws.s, kb, hf, lane);
+}
+
+// Iteration t.  PAR = t mod 2 names the buffers statically: tile t is read
+// from kbuf[PAR] / vbuf[PAR]; tile t+1 is loaded into registers first and
+// written to kbuf[PAR ^ 1] / vbuf[PAR ^ 1] at the end.
+template <class Tr, int PAR, bool kMasked>
+__device__ inline void step_tile(WaveState<Tr>& ws, const StepParams& p, const TilePlan& tp, TileStage<Tr>* st,
+                                 int t, int b, int g, const long long* qg, RA_LDS char* const* kbuf,
+                                 RA_LDS char* const* vbuf, int lane) {
+  const KTile ti = tp.tile(p, t);
+  const bool more = t + 1 < tp.n;
+  if (more) {
+    const KTile t1 = tp.tile(p, t + 1);
+    st[0].load(p, b, g, t1, false);
+    st[0].load(p, b, g, t1, true);
+  }
+#pragma unroll
+  for (int kb = 0; kb < kKB; ++kb) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) ws.s[kb][qb] = f32x16{};
+#pragma unroll
+    for (int u = 0; u < Tr::kSUnits; ++u) Tr::s_unit(ws.s[kb], kbuf[PAR], kb, u, ws.qf, lane);
+  }
+  float mb[kQB], lsum[kQB];
+  softmax_prep<Tr, kMasked>(ws, p, ti, qg, lane, mb);
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) lsum[qb] = 0.f;
+#pragma unroll
+  for (int grp = 0; grp < 2 * kKB; ++grp)
+    softmax_pv_group<Tr>(ws, p, grp, mb, lsum, vbuf[PAR], lane);
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) ws.l_part[qb] += lsum[qb];
+  if (more) {
+    st[0].store_k(kbuf[PAR ^ 1]);
+    st[0].store_v(vbuf[PAR ^ 1]);
+  }
+  __syncthreads();
+}
+
+template <class Tr>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
+void attn_step_kernel(StepParams p) {
   constexpr int D = Tr::D;
   constexpr int kTileBytes = kBK * Tr::kRowBytes;
-  __shared__ __attribute__((aligned(16))) char smem_raw[4 * kTileBytes];
-  RA_LDS char* smem = (RA_LDS char*)smem_raw;
+  // Two K and two V tile buffers, as distinct arrays.
+  __shared__ __attribute__((aligned(16))) char k0_raw[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char k1_raw[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char v0_raw[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char v1_raw[kTileBytes];
+  RA_LDS char* const kbuf[2] = {(RA_LDS char*)k0_raw, (RA_LDS char*)k1_raw};
+  RA_LDS char* const vbuf[2] = {(RA_LDS char*)v0_raw, (RA_LDS char*)v1_raw};
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -300,25 +476,9 @@ __global__ __launch_bounds__(256) void attn_step_kernel(StepParams p) {
   const long long qglob0 = p.qs_start[qs] + q_in;
   const long long qglob_last = qglob0 + qrows - 1;
 
-  // --- key tiles with at least one key visible to some row of the tile
-  int nt[2] = {0, 0};
-  long long khi[2] = {0, 0};
-  for (int s = 0; s < p.nks; ++s) {
-    long long hi = p.ks_len[s];
-    if (p.causal) hi = min(hi, qglob_last + 1 - p.ks_start[s]);
-    hi = max(hi, 0LL);
-    khi[s] = hi;
-    nt[s] = (int)((hi + kBK - 1) / kBK);
-  }
-  const int ntiles = nt[0] + nt[1];
+  const TilePlan tp = plan_tiles(p, qglob0, qglob_last);
 
-  const int n = lane & 31;
-  const int wrow = wave * 32 + n;
-  const bool row_ok = wrow < qrows;
-  const long long qg = qglob0 + wrow;
-  const long long orow = ((long long)b * p.Sq + qlocal0 + wrow) * p.Hq + h;  // (b, row, h)
-
-  if (ntiles == 0) {
+  if (tp.n == 0) {
     // INIT of rows that see no key of this block: the merge identity.
     if (!p.accum) {
       for (int i = threadIdx.x; i < qrows * (D / 4); i += kThreads) {
@@ -331,139 +491,103 @@ __global__ __launch_bounds__(256) void attn_step_kernel(StepParams p) {
     return;
   }
 
-  typename Tr::QFrag qf;
-  Tr::load_q(qf, (const typename Tr::Elem*)p.q + orow * D, row_ok, lane);
-
-  f32x16 oacc[D / 32];
+  // This lane's query rows: row 32 kQB wave + 32 qb + lane % 32 of the work item.
+  bool row_ok[kQB];
+  long long qg[kQB], orow[kQB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  float m_ref = kNegInf;  // reference maximum of the raw (unscaled) scores
-  float l_part = 0.f;     // this lane's share of the row sum
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int wrow = 32 * kQB * wave + 32 * qb + (lane & 31);
+    row_ok[qb] = wrow < qrows;
+    qg[qb] = qglob0 + wrow;
+    orow[qb] = ((long long)b * p.Sq + qlocal0 + wrow) * p.Hq + h;  // (b, row, h)
+  }
 
-  const bool wave_rows = wave * 32 < qrows;
-  const long long wq0 = qglob0 + wave * 32;                    // wave's first query
-  const long long wq1 = qglob0 + min(wave * 32 + 31, qrows - 1);  // and last
+  TileStage<Tr> st[1];
+  st[0].init(p);
 
-  Stage<Tr> st;
-  st.load(p, b, g, key_tile(p, nt, khi, 0));
-  st.store(smem, smem + kTileBytes);
+  // --- prologue: tile 0 in flight while Q is read
+  st[0].load(p, b, g, tp.tile(p, 0), false);
+  st[0].load(p, b, g, tp.tile(p, 0), true);
+  WaveState<Tr> ws;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    Tr::load_q(ws.qf, qb, (const typename Tr::Elem*)p.q + orow[qb] * D, row_ok[qb], lane);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) ws.o[db][qb] = f32x16{};
+    ws.m_ref[qb] = kNegInf;
+    ws.l_part[qb] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) ws.s[kb][qb] = f32x16{};
+  }
+  st[0].store_k(kbuf[0]);
+  st[0].store_v(vbuf[0]);
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const RA_LDS char* kt = smem + buf * 2 * kTileBytes;
-    const RA_LDS char* vt = kt + kTileBytes;
-    if (t + 1 < ntiles) st.load(p, b, g, key_tile(p, nt, khi, t + 1));
-
-    const KTile ti = key_tile(p, nt, khi, t);
-    const bool skip = !wave_rows || (p.causal && ti.glob0 > wq1);
-    if (!skip) {
-      f32x16 sacc[2];
-      sacc[0] = Tr::s_block(kt, 0, qf, lane);
-      sacc[1] = Tr::s_block(kt, 1, qf, lane);
-      const bool need_mask = ti.count < kBK || (p.causal && ti.glob0 + kBK - 1 > wq0);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * kb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const bool vis = key < ti.count && (!p.causal || ti.glob0 + key <= qg);
-            if (!vis) sacc[kb][r] = kNegInf;
-          }
-        }
-      }
-      float tmax = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kb][r]);
-      }
-      tmax = max_halves(tmax);
-      const float m_new = fmaxf(m_ref, tmax);
-      // -inf reference: the difference is +inf and the maximum is taken;
-      // both -inf: NaN compares false and nothing moves.
-      const bool grow = (m_new - m_ref) * p.sl2 > kTau;
-      float alpha = 1.f;
-      if (grow) {
-        alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * p.sl2);
-        m_ref = m_new;
-      }
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-        l_part *= alpha;
-      }
-      const float mb = m_ref == kNegInf ? 0.f : m_ref * p.sl2;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], p.sl2, -mb));
-          sacc[kb][r] = pr;
-          lsum += pr;
-        }
-      }
-      l_part += lsum;
-      Tr::pv(oacc, vt, sacc, lane);
-    }
-
-    if (t + 1 < ntiles) {
-      RA_LDS char* kn = smem + (buf ^ 1) * 2 * kTileBytes;
-      st.store(kn, kn + kTileBytes);
-    }
-    __syncthreads();
+  // --- main loop: tiles every row sees, unrolled by two so that buffers
+  // are named statically, then the masked tiles (no mask code runs on the
+  // former).  Iteration t uses parity t mod 2 in both loops.
+  int t = 0;
+  for (; t + 1 < tp.n_full; t += 2) {
+    step_tile<Tr, 0, false>(ws, p, tp, st, t, b, g, qg, kbuf, vbuf, lane);
+    step_tile<Tr, 1, false>(ws, p, tp, st, t + 1, b, g, qg, kbuf, vbuf, lane);
+  }
+  if (t < tp.n_full) step_tile<Tr, 0, false>(ws, p, tp, st, t++, b, g, qg, kbuf, vbuf, lane);
+  for (; t < tp.n; ++t) {
+    if (t & 1)
+      step_tile<Tr, 1, true>(ws, p, tp, st, t, b, g, qg, kbuf, vbuf, lane);
+    else
+      step_tile<Tr, 0, true>(ws, p, tp, st, t, b, g, qg, kbuf, vbuf, lane);
   }
 
   // --- epilogue: normalise, then store (INIT) or merge into HBM (ACCUM)
-  const float l_tot = sum_halves(l_part);
-  if (!row_ok) return;
-  float* orow_ptr = p.o + orow * D;
   const int dsub = 4 * (lane >> 5);
-  if (l_tot > 0.f) {
-    const float inv = 1.f / l_tot;
-    const float lse_s = m_ref * p.scale + __builtin_amdgcn_logf(l_tot) * kLn2;
-    float lse_r = kNegInf;
-    if (p.accum) lse_r = p.lse[orow];
-    if (lse_r == kNegInf) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
+  for (int qb = 0; qb < kQB; ++qb) {
+    const float l_tot = sum_halves(ws.l_part[qb]);
+    if (!row_ok[qb]) continue;
+    float* orow_ptr = p.o + orow[qb] * D;
+    if (l_tot > 0.f) {
+      const float inv = 1.f / l_tot;
+      const float lse_s = ws.m_ref[qb] * p.scale + __builtin_amdgcn_logf(l_tot) * kLn2;
+      float lse_r = kNegInf;
+      if (p.accum) lse_r = p.lse[orow[qb]];
+      if (lse_r == kNegInf) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float4 v = {oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv,
-                      oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv};
-          *(float4*)(orow_ptr + 32 * db + 8 * j + dsub) = v;
-        }
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x16& a = ws.o[db][qb];
+            const float4 v = {a[4 * j] * inv, a[4 * j + 1] * inv, a[4 * j + 2] * inv, a[4 * j + 3] * inv};
+            *(float4*)(orow_ptr + 32 * db + 8 * j + dsub) = v;
+          }
+        if (lane < 32) p.lse[orow[qb]] = lse_s;
+      } else {
+        const float m = fmaxf(lse_r, lse_s);
+        const float wr = __builtin_amdgcn_exp2f((lse_r - m) * kLog2e);
+        const float wsum = __builtin_amdgcn_exp2f((lse_s - m) * kLog2e);
+        const float den = wr + wsum;
+        const float cr = wr / den;
+        const float cs = wsum / den * inv;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x16& a = ws.o[db][qb];
+            float* ptr = orow_ptr + 32 * db + 8 * j + dsub;
+            const float4 r = *(const float4*)ptr;
+            const float4 v = {cr * r.x + cs * a[4 * j], cr * r.y + cs * a[4 * j + 1],
+                              cr * r.z + cs * a[4 * j + 2], cr * r.w + cs * a[4 * j + 3]};
+            *(float4*)ptr = v;
+          }
+        if (lane < 32) p.lse[orow[qb]] = m + __builtin_amdgcn_logf(den) * kLn2;
       }
-      if (lane < 32) p.lse[orow] = lse_s;
-    } else {
-      const float m = fmaxf(lse_r, lse_s);
-      const float wr = __builtin_amdgcn_exp2f((lse_r - m) * kLog2e);
-      const float ws = __builtin_amdgcn_exp2f((lse_s - m) * kLog2e);
-      const float den = wr + ws;
-      const float cr = wr / den;
-      const float cs = ws / den * inv;
+    } else if (!p.accum) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float* ptr = orow_ptr + 32 * db + 8 * j + dsub;
-          const float4 r = *(const float4*)ptr;
-          float4 v = {cr * r.x + cs * oacc[db][4 * j], cr * r.y + cs * oacc[db][4 * j + 1],
-                      cr * r.z + cs * oacc[db][4 * j + 2], cr * r.w + cs * oacc[db][4 * j + 3]};
-          *(float4*)ptr = v;
-        }
-      }
-      if (lane < 32) p.lse[orow] = m + __builtin_amdgcn_logf(den) * kLn2;
+        for (int j = 0; j < 4; ++j) *(float4*)(orow_ptr + 32 * db + 8 * j + dsub) = float4{0.f, 0.f, 0.f, 0.f};
+      if (lane < 32) p.lse[orow[qb]] = kNegInf;
     }
-  } else if (!p.accum) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *(float4*)(orow_ptr + 32 * db + 8 * j + dsub) = float4{0.f, 0.f, 0.f, 0.f};
-    }
-    if (lane < 32) p.lse[orow] = kNegInf;
   }
 }
 

@@ -8,7 +8,7 @@ namespace ra {
 
 // Query rows per workgroup (4 waves x 32 rows) and keys per LDS tile.
 constexpr int kBQ = 128;
-constexpr int kBK = 64;
+constexpr int kBK = 32;
 
 // Everything one launch of the attention step kernel needs.  Spans are the
 // (at most two) query / key spans of the step in local row order; only query
