@@ -33,8 +33,9 @@
 //   in-lane reductions plus one lane swap across the two halves.
 //   O^T += V^T P^T on MFMA: P^T is the exponentiated accumulator itself (bf16
 //   rounded for the bf16 path), with the MFMA's reduction index mapped onto the
-//   keys in the order the accumulator holds them; V^T is read from row-major V
-//   in LDS with the transposing LDS read (bf16) or scalar reads (f32).
+//   keys in the order the accumulator holds them.  The bf16 path stages V
+//   transposed in LDS, keys permuted into that same order, so each V^T operand
+//   is one 16-byte LDS read; the f32 path keeps V row-major and reads scalars.
 //   The softmax runs in base 2 (exp2 of scale*log2(e)-scaled scores) in fp32.
 //   The running maximum is only moved when it grows by more than 2^8 in the
 //   exponent, so the O rescale is skipped on most tiles; probabilities stay
@@ -125,12 +126,66 @@ struct Bf16 {
       acc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.f[qb][u], acc[qb], 0, 0, 0);
   }
 
+  // V is staged into LDS transposed: row d (64 bytes) holds the 32 keys of
+  // the tile in the order the S^T accumulator holds them,
+  //   pos(k) = 16 (k / 16) + 8 ((k / 4) % 2) + 4 ((k / 8) % 2) + k % 4,
+  // i.e. bits 2 and 3 of k swapped.  The 8 keys one lane feeds to a P V MFMA
+  // are then 16 contiguous bytes (one ds_read_b128).  The 16-byte chunk pos/8
+  // of row d sits at chunk ^ (((d >> 2) ^ (d >> 4)) & 3), conflict-free for
+  // both the reads (16 consecutive rows) and the writes (8 rows x 4 chunks).
+  static_assert(kBK == 32, "V^T rows hold one 32-key tile");
+  __device__ static unsigned vt_swz(unsigned d) { return ((d >> 2) ^ (d >> 4)) & 3u; }
+  __device__ static unsigned vt_pos(unsigned k) {
+    return (k & ~15u) | (((k >> 2) & 1u) << 3) | (((k >> 3) & 1u) << 2) | (k & 3u);
+  }
+
+  // Staging of one V tile: thread t takes keys 2m, 2m+1 (m = t % 16) at
+  // d-chunk c = t / 16 (8 values of d), packs each (V[2m][d], V[2m+1][d])
+  // into a dword and writes the 8 dwords to rows 8c .. 8c+7 of V^T.
+  struct VStage {
+    u32x4 ra, rb;
+    unsigned goff;       // global byte offset of (row 2m, chunk c) in a full tile
+    unsigned wbase[2];   // LDS byte offset for rows 8c + 4h, h = 0, 1
+    bool active;
+
+    __device__ void init(unsigned row_bytes) {
+      const unsigned m = threadIdx.x % 16, c = threadIdx.x / 16;
+      active = c < D / 8;
+      goff = 2 * m * row_bytes + c * 16;
+      const unsigned pos = vt_pos(2 * m);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned d = 8 * c + 4 * h;
+        wbase[h] = d * 64 + (((pos >> 3) ^ vt_swz(d)) * 16) + (pos & 7) * 2;
+      }
+    }
+    __device__ void load(const char* src, int count, unsigned row_bytes) {
+      if (!active) return;
+      const unsigned m = threadIdx.x % 16, c = threadIdx.x / 16;
+      if (count == kBK) {
+        ra = *(const u32x4*)(src + goff);
+        rb = *(const u32x4*)(src + goff + row_bytes);
+      } else {
+        ra = *(const u32x4*)(src + min((int)(2 * m), count - 1) * row_bytes + c * 16);
+        rb = *(const u32x4*)(src + min((int)(2 * m + 1), count - 1) * row_bytes + c * 16);
+      }
+    }
+    __device__ void store(RA_LDS char* dst) const {
+      if (!active) return;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const unsigned x = ra[j >> 1], y = rb[j >> 1];
+        const unsigned w = (j & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+        *(RA_LDS unsigned*)(dst + wbase[j >> 2] + (j & 3) * 64) = w;
+      }
+    }
+  };
+
   // O^T[db][qb] += V^T P^T over the 16 keys 32kb + 16hf + [0, 16) of the
   // tile.  The MFMA consumes accumulator registers 8hf..8hf+7 of S^T block kb
   // (already exponentiated, rounded to bf16 here), i.e. reduction index
-  // 8(l/32)+e <-> key 32kb + 16hf + 8(e/4) + 4(l/32) + e%4; the V^T operand is
-  // gathered with two transposing reads of 4 keys x 16 columns per 16-lane
-  // group and feeds both query blocks.
+  // 8(l/32)+e <-> key 32kb + 16hf + 8(e/4) + 4(l/32) + e%4; V^T row
+  // 32db + l%32 holds exactly those keys at chunk 2hf + l/32.
   __device__ static void pv_group(f32x16 (*o)[kQB], const RA_LDS char* vt, const f32x16 (*p)[kQB], int kb,
                                   int hf, int lane) {
     bf16x8 pb[kQB];
@@ -141,17 +196,11 @@ struct Bf16 {
       for (int e = 0; e < 8; ++e) x[e] = p[kb][qb][8 * hf + e];
       pb[qb] = __builtin_convertvector(x, bf16x8);
     }
-    const int gi = lane >> 4, s = lane & 15;
-    const unsigned r1 = 32 * kb + 16 * hf + 4 * (gi >> 1) + (s >> 2);
-    const unsigned r2 = r1 + 8;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const unsigned d = 32 * db + 16 * (gi & 1) + 4 * (s & 3);
-      const unsigned o1 = r1 * kRowBytes + (((d >> 3) ^ swz_v<kCPR>(r1)) * 16) + (d & 7) * 2;
-      const unsigned o2 = r2 * kRowBytes + (((d >> 3) ^ swz_v<kCPR>(r2)) * 16) + (d & 7) * 2;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vt + o1));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vt + o2));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      const unsigned d = 32 * db + (lane & 31);
+      const unsigned chunk = 2 * (16 * kb + 8 * hf) / 8 + (lane >> 5);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(vt, d * 64 + ((chunk ^ vt_swz(d)) * 16)));
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb)
         o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb], o[db][qb], 0, 0, 0);
@@ -185,6 +234,34 @@ struct F32 {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) acc[qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, q.f[qb][u], acc[qb], 0, 0, 0);
   }
+
+  // V is staged row-major with the V swizzle (read back with scalar reads).
+  struct VStage {
+    static constexpr int kPer = kBK * kCPR / kThreads;
+    u32x4 r[kPer];
+    unsigned goff[kPer], woff[kPer];
+    __device__ void init(unsigned row_bytes) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const unsigned idx = threadIdx.x + i * kThreads;
+        const unsigned row = idx / kCPR, c = idx % kCPR;
+        goff[i] = row * row_bytes + c * 16;
+        woff[i] = row * kRowBytes + ((c ^ swz_v<kCPR>(row)) * 16);
+      }
+    }
+    __device__ void load(const char* src, int count, unsigned row_bytes) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const unsigned idx = threadIdx.x + i * kThreads;
+        const unsigned row = idx / kCPR, c = idx % kCPR;
+        r[i] = *(const u32x4*)(src + (count == kBK ? goff[i] : min((int)row, count - 1) * row_bytes + c * 16));
+      }
+    }
+    __device__ void store(RA_LDS char* dst) const {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) *(RA_LDS u32x4*)(dst + woff[i]) = r[i];
+    }
+  };
 
   // MFMA (kb, j) pairs reduction index l/32 with key 32kb + 8(j/4) + 4(l/32) + j%4,
   // which is the key accumulator register j of lane l holds; group hf covers
@@ -285,10 +362,11 @@ __device__ inline TilePlan plan_tiles(const StepParams& p, long long qglob0, lon
 template <class Tr>
 struct TileStage {
   static constexpr int kPer = kBK * Tr::kCPR / kThreads;
-  u32x4 k[kPer], v[kPer];
-  unsigned goff[kPer];             // global byte offset of each chunk in a full tile
-  unsigned koff[kPer], voff[kPer];  // its swizzled LDS byte offset
-  unsigned row_bytes;              // global stride between key rows
+  u32x4 k[kPer];
+  unsigned goff[kPer];   // global byte offset of each K chunk in a full tile
+  unsigned koff[kPer];   // its swizzled LDS byte offset
+  unsigned row_bytes;    // global stride between key rows
+  typename Tr::VStage vs;
 
   __device__ void init(const StepParams& p) {
     row_bytes = (unsigned)(p.Hkv * Tr::D * (int)sizeof(typename Tr::Elem));
@@ -298,24 +376,27 @@ struct TileStage {
       const unsigned row = idx / Tr::kCPR, c = idx % Tr::kCPR;
       goff[i] = row * row_bytes + c * 16;
       koff[i] = row * Tr::kRowBytes + ((c ^ swz_k<Tr::kCPR>(row)) * 16);
-      voff[i] = row * Tr::kRowBytes + ((c ^ swz_v<Tr::kCPR>(row)) * 16);
     }
+    vs.init(row_bytes);
   }
 
   // Loads tile kt of K (is_v false) or V into the staging registers.
   __device__ void load(const StepParams& p, int b, int g, const KTile& kt, bool is_v) {
     const long long base = (((long long)b * p.Sk + kt.local0) * p.Hkv + g) * (long long)(Tr::D * sizeof(typename Tr::Elem));
-    const char* src = (const char*)(is_v ? p.v : p.k) + base;
-    u32x4* dst = is_v ? v : k;
+    if (is_v) {
+      vs.load((const char*)p.v + base, kt.count, row_bytes);
+      return;
+    }
+    const char* src = (const char*)p.k + base;
     if (kt.count == kBK) {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) dst[i] = *(const u32x4*)(src + goff[i]);
+      for (int i = 0; i < kPer; ++i) k[i] = *(const u32x4*)(src + goff[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const unsigned idx = threadIdx.x + i * kThreads;
         const unsigned row = idx / Tr::kCPR, c = idx % Tr::kCPR;
-        dst[i] = *(const u32x4*)(src + min((int)row, kt.count - 1) * row_bytes + c * 16);
+        k[i] = *(const u32x4*)(src + min((int)row, kt.count - 1) * row_bytes + c * 16);
       }
     }
   }
@@ -324,10 +405,7 @@ struct TileStage {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) *(RA_LDS u32x4*)(dst + koff[i]) = k[i];
   }
-  __device__ void store_v(RA_LDS char* dst) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) *(RA_LDS u32x4*)(dst + voff[i]) = v[i];
-  }
+  __device__ void store_v(RA_LDS char* dst) const { vs.store(dst); }
 };
 
 // Per-wave state carried across key tiles.
