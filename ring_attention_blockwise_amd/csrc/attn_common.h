@@ -1,0 +1,217 @@
+// Device code shared by the attention step kernels: wave reductions, the key
+// tile plan of a work item, the work-item decode and the epilogue that stores
+// (INIT) or merges (ACCUM) a work item's normalised output and log-sum-exp.
+//
+// Accumulator layout used throughout: a 32x32 MFMA accumulator puts row
+// 8(r/4) + 4(l/32) + r%4, column l%32 in register r of lane l.  The kernels
+// compute transposed products, so a column is a query row and each lane owns
+// one query of every 32-row block (lanes l and l+32 share it).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ra_internal.h"
+
+#define RA_LDS __attribute__((address_space(3)))
+
+namespace ra {
+namespace dev {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// The reference maximum of a row only moves when probabilities would exceed
+// 2^kTau, so most tiles skip the rescale of O; the final division by the row
+// sum makes the result independent of where the reference sits.
+constexpr float kTau = 8.0f;
+
+__device__ inline float max_halves(float x) {
+  // v_permlane32_swap with both operands x: every lane sees x of lane ^ 32 in
+  // one of the two results; max/sum of both is symmetric.
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline u32x4 lds_load16(const RA_LDS char* base, unsigned off) {
+  return *(const RA_LDS u32x4*)(base + off);
+}
+
+// ---------------------------------------------------------------------------
+// Key tiles of one work item.  Tiles restart at each key span.  Within a span
+// the tiles whose keys are all visible to every query row of the work item
+// come first and run no mask code; the rest (on the causal diagonal, or cut
+// short by the span's end) follow and are masked.  The order of the tiles does
+// not change the result.
+struct KTile {
+  long long local0;  // first local key row
+  long long glob0;   // its global position
+  int count;         // rows that exist and may be visible (<= kBK)
+};
+
+struct TilePlan {
+  int nf[2], nr[2];  // full and masked tiles per span
+  long long hi[2];   // keys of the span visible to the work item's last row
+  int n_full, n;
+
+  __device__ KTile tile(const StepParams& p, int t) const {
+    int s;
+    long long kin;
+    if (t < n_full) {
+      s = t < nf[0] ? 0 : 1;
+      kin = (long long)(s ? t - nf[0] : t) * kBK;
+    } else {
+      const int u = t - n_full;
+      s = u < nr[0] ? 0 : 1;
+      kin = (long long)(nf[s] + (s ? u - nr[0] : u)) * kBK;
+    }
+    KTile kt;
+    kt.local0 = p.ks_off[s] + kin;
+    kt.glob0 = p.ks_start[s] + kin;
+    kt.count = (int)min((long long)kBK, hi[s] - kin);
+    return kt;
+  }
+};
+
+__device__ inline TilePlan plan_tiles(const StepParams& p, long long qglob0, long long qglob_last) {
+  TilePlan tp;
+  tp.n_full = 0;
+  tp.n = 0;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    long long hi = 0, full = 0;
+    if (s < p.nks) {
+      hi = p.ks_len[s];
+      full = hi;
+      if (p.causal) {
+        hi = min(hi, qglob_last + 1 - p.ks_start[s]);   // keys <= the last row
+        full = min(hi, qglob0 + 1 - p.ks_start[s]);     // keys <= the first row
+      }
+      hi = max(hi, 0LL);
+      full = max(full, 0LL);
+    }
+    tp.hi[s] = hi;
+    tp.nf[s] = (int)(full / kBK);
+    tp.nr[s] = (int)((hi - (long long)tp.nf[s] * kBK + kBK - 1) / kBK);
+    tp.n_full += tp.nf[s];
+    tp.n += tp.nf[s] + tp.nr[s];
+  }
+  return tp;
+}
+
+// ---------------------------------------------------------------------------
+// Work item of a workgroup: BQ consecutive query rows of one (batch, query
+// head).  XCD x (= block id mod 8, dispatch is round-robin over the 8 XCDs)
+// takes a contiguous run of work items, ordered kv-head major so the query
+// tiles that read one K/V head share that XCD's L2, heavier (later) query
+// tiles first.
+struct WorkItem {
+  int b, g, h;
+  int qrows;            // rows of the work item that exist (<= BQ)
+  long long qlocal0;    // first local query row
+  long long qglob0;     // its global position
+};
+
+template <int BQ>
+__device__ inline bool decode_work(const StepParams& p, WorkItem& wi) {
+  const int w = (blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
+  if (w >= p.n_work) return false;
+  const int qt_rev = w % p.n_qtiles;
+  int rest = w / p.n_qtiles;
+  const int hh = rest % p.G;
+  rest /= p.G;
+  wi.g = rest % p.Hkv;
+  wi.b = rest / p.Hkv;
+  wi.h = wi.g * p.G + hh;
+  const int qt = p.n_qtiles - 1 - qt_rev;
+  const int qs = qt < p.qt_span0 ? 0 : 1;
+  const long long q_in = (long long)(qs ? qt - p.qt_span0 : qt) * BQ;
+  wi.qrows = (int)min((long long)BQ, p.qs_len[qs] - q_in);
+  wi.qlocal0 = p.qs_off[qs] + q_in;
+  wi.qglob0 = p.qs_start[qs] + q_in;
+  return true;
+}
+
+// INIT of a work item whose rows see no key of the block: the merge identity
+// (O = 0, LSE = -inf).  ACCUM leaves such rows untouched.
+template <int D, int THREADS>
+__device__ inline void store_identity(const StepParams& p, const WorkItem& wi) {
+  if (p.accum) return;
+  for (int i = threadIdx.x; i < wi.qrows * (D / 4); i += THREADS) {
+    const int r = i / (D / 4), c = i % (D / 4);
+    const long long orr = ((long long)wi.b * p.Sq + wi.qlocal0 + r) * p.Hq + wi.h;
+    *(float4*)(p.o + orr * D + 4 * c) = float4{0.f, 0.f, 0.f, 0.f};
+    if (c == 0) p.lse[orr] = kNegInf;
+  }
+}
+
+// Epilogue of 32-row block qb held by a wave: O^T accumulators oq[D/32][qb]
+// (already complete over the block's keys), the reference maximum m_ref of
+// the raw scores and this lane's share of the row sum.  INIT stores O / l and
+// the LSE; ACCUM merges them into the (O, LSE) already in HBM (a stored LSE of
+// -inf is the identity and is replaced); a row that saw no visible key stores
+// the identity in INIT and is left alone in ACCUM.
+template <int D, int NQB>
+__device__ inline void finish_rows(const StepParams& p, const f32x16 (*oq)[NQB], int qb, float m_ref, float l_part,
+                                   bool row_ok, long long orow, int lane) {
+  const int dsub = 4 * (lane >> 5);
+  const float l_tot = sum_halves(l_part);
+  if (!row_ok) return;
+  float* orow_ptr = p.o + orow * D;
+  if (l_tot > 0.f) {
+    const float inv = 1.f / l_tot;
+    const float lse_s = m_ref * p.scale + __builtin_amdgcn_logf(l_tot) * kLn2;
+    float lse_r = kNegInf;
+    if (p.accum) lse_r = p.lse[orow];
+    if (lse_r == kNegInf) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x16& a = oq[db][qb];
+          const float4 v = {a[4 * j] * inv, a[4 * j + 1] * inv, a[4 * j + 2] * inv, a[4 * j + 3] * inv};
+          *(float4*)(orow_ptr + 32 * db + 8 * j + dsub) = v;
+        }
+      if (lane < 32) p.lse[orow] = lse_s;
+    } else {
+      const float m = fmaxf(lse_r, lse_s);
+      const float wr = __builtin_amdgcn_exp2f((lse_r - m) * kLog2e);
+      const float wsum = __builtin_amdgcn_exp2f((lse_s - m) * kLog2e);
+      const float den = wr + wsum;
+      const float cr = wr / den;
+      const float cs = wsum / den * inv;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x16& a = oq[db][qb];
+          float* ptr = orow_ptr + 32 * db + 8 * j + dsub;
+          const float4 r = *(const float4*)ptr;
+          const float4 v = {cr * r.x + cs * a[4 * j], cr * r.y + cs * a[4 * j + 1], cr * r.z + cs * a[4 * j + 2],
+                            cr * r.w + cs * a[4 * j + 3]};
+          *(float4*)ptr = v;
+        }
+      if (lane < 32) p.lse[orow] = m + __builtin_amdgcn_logf(den) * kLn2;
+    }
+  } else if (!p.accum) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *(float4*)(orow_ptr + 32 * db + 8 * j + dsub) = float4{0.f, 0.f, 0.f, 0.f};
+    if (lane < 32) p.lse[orow] = kNegInf;
+  }
+}
+
+}  // namespace dev
+}  // namespace ra

@@ -1,0 +1,358 @@
+// One ring step of blockwise attention on gfx950 for bf16 inputs, with the
+// log-sum-exp merge fused into the epilogue.
+//
+// What it computes (DeDLOC guide, "Step 3" and "3. Online Softmax Rescaling
+// Across Decentralized Ranks"; causal skipping from its "Best Practices" row
+// "Causal Mask Handling"): for every query row of the rank's fixed block and
+// the key/value block that arrived at this ring step, the partial output
+// O = softmax(scale * q K^T) V over the visible keys and its log-sum-exp; in
+// INIT mode that pair is stored, in ACCUM mode it is merged into the running
+// (O, LSE) held in HBM.
+//
+// Work decomposition
+//   * A workgroup (4 waves, one per SIMD) owns 256 consecutive query rows of
+//     one (batch, query head); wave w owns rows [64w, 64w + 64) as two 32-row
+//     blocks.  Every K or V operand a wave reads from LDS feeds the MFMAs of
+//     both blocks, which halves the LDS read traffic per flop against 32 rows
+//     per wave: LDS, not the matrix cores, is the tighter limit of this loop
+//     otherwise.  Two workgroups share a CU, so each SIMD interleaves two
+//     waves: while one runs its softmax on the vector ALUs, the other issues
+//     MFMAs.
+//   * Keys are processed in tiles of 32, double-buffered in LDS.  Both tiles
+//     are copied global -> LDS by the load unit itself (buffer loads with the
+//     LDS bit, 16 bytes per lane), so staging takes no registers and no LDS
+//     store instructions.  Tile t+1 is started at the top of iteration t and
+//     waited for just before the barrier that ends it, so its latency hides
+//     behind a whole tile of work.
+//   * Only key tiles with at least one visible key are visited; tiles all of
+//     whose keys every row of the work item sees run first and skip the mask.
+//
+// Per-wave math (64 queries x 32 keys per tile)
+//   S^T = K Q^T on 32x32x16 MFMAs.  Lane l feeds the K row sigma(l % 32),
+//   sigma swapping bits 2 and 3 of the row index, which makes register r of
+//   lane l hold key 16(r/8) + 8(l/32) + r%8 of query l%32.  Row max and row
+//   sum are in-lane reductions plus one swap of the two lane halves.
+//   O^T += V^T P^T on 32x32x16 MFMAs, 16 keys per MFMA: accumulator registers
+//   8h .. 8h+7 of lane l, exponentiated and rounded to bf16, are the B
+//   operand of keys 16h + [0, 16) in natural order; the A operand (8
+//   consecutive keys of one column d of V per lane) comes from the row-major
+//   V tile through two transposing LDS reads (ds_read_b64_tr_b16).
+//   The softmax runs in base 2 (exp2 of scale*log2(e)-scaled scores) in fp32
+//   with a lazily moved reference maximum.
+#include "attn_common.h"
+
+namespace ra {
+namespace {
+
+using namespace dev;
+
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kQB = 2;         // 32-row query blocks per wave
+static_assert(kBQBf16 == 4 * 32 * kQB, "workgroup rows");
+static_assert(kBK == 32, "one 32x32 score block per query block and tile");
+
+template <int D>
+struct Layout {
+  static constexpr int kRowBytes = 2 * D;   // a key row in HBM
+  static constexpr int kCPR = kRowBytes / 16;
+  // K tile in LDS: 32 rows of 2D bytes; 16-byte chunk c of row r sits at
+  // chunk c ^ ksw(r), so the 16 rows one operand read touches per pass land
+  // in distinct banks.
+  static constexpr int kKStride = kRowBytes;
+  static constexpr int kKTileBytes = kBK * kKStride;
+  // V tile in LDS: 32 rows, padded by 64 bytes so that the 4 rows one
+  // transposing read touches per pass start 64 bytes apart modulo the 256
+  // bytes of the banks.
+  static constexpr int kVStride = kRowBytes + 64;
+  static constexpr int kVTileBytes = kBK * kVStride;
+  // DMA: one instruction writes 64 consecutive 16-byte slots (1 KiB).
+  static constexpr int kKDma = kKTileBytes / 1024;
+  static constexpr int kVDma = kVTileBytes / 1024;
+  static_assert(kKTileBytes % 1024 == 0 && kVTileBytes % 1024 == 0, "whole DMA instructions");
+  static_assert(kKDma % 4 == 0, "K instructions split evenly over the 4 waves");
+
+  __device__ static unsigned ksw(unsigned r) { return (kCPR == 16 ? r : r >> 1) & (kCPR - 1); }
+};
+
+__device__ inline unsigned sigma(unsigned i) { return (i & ~12u) | ((i & 4u) << 1) | ((i & 8u) >> 1); }
+
+template <int D>
+struct WaveState {
+  bf16x8 q[kQB][D / 16];      // Q^T operands: Q[row][16u + 8(l/32) .. +7]
+  f32x16 o[D / 32][kQB];      // O^T accumulators
+  float m_ref[kQB];           // reference maximum of the raw scores
+  float l_part[kQB];          // this lane's share of the row sum
+};
+
+// Per-thread addresses.  They are cheap to derive from the thread id, so each
+// tile derives them again from a laundered copy of it instead of keeping them
+// in registers across the loop.
+template <int D>
+struct Lane {
+  typedef Layout<D> Ly;
+  unsigned lane, row_bytes;
+  int wave;
+
+  __device__ Lane(unsigned row_bytes_, int wave_) : row_bytes(row_bytes_), wave(wave_) {
+    unsigned tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    lane = tid & 63u;
+  }
+  // K operand read of unit u: kb0() ^ 32u (row sigma(l % 32), chunk 2u + l/32)
+  __device__ unsigned kb0() const {
+    const unsigned rho = sigma(lane & 31u);
+    return (rho * Ly::kKStride) | (16u * (Ly::ksw(rho) ^ (lane >> 5)));
+  }
+  // Transposing V reads.  In each 16-lane group g (lanes 16g + s) lane s
+  // addresses key row 8(g/2) + s/4 (+16h for key half h, +4 for the second
+  // read) at column d = 32db + 16(g%2) + 4(s%4); the read hands lane s
+  // element s%4 of the chunk of lane 4j + s/4 as its element j, i.e. column
+  // 32db + 16(g%2) + s of key rows +j: the A operand of the PV MFMA.
+  __device__ unsigned vb0() const {
+    const unsigned g = lane >> 4, s = lane & 15u;
+    return (8u * (g >> 1) + (s >> 2)) * Ly::kVStride + 2u * (16u * (g & 1u) + 4u * (s & 3u));
+  }
+  // Tile offsets of the chunks this lane copies.  K slot s holds row
+  // s / kCPR, chunk (s % kCPR) ^ ksw(row).  V slot s holds row s / (kVStride
+  // / 16), chunk s % (kVStride / 16); chunks past kCPR are padding and load
+  // from past the record (zeros).
+  __device__ unsigned kgo(int i) const {
+    const unsigned slot = (wave * (Ly::kKDma / 4) + i) * 64 + lane;
+    const unsigned r = slot / Ly::kCPR;
+    return r * row_bytes + 16u * ((slot % Ly::kCPR) ^ Ly::ksw(r));
+  }
+  __device__ unsigned vgo(int ins) const {
+    constexpr unsigned spr = Ly::kVStride / 16;
+    const unsigned slot = ins * 64 + lane;
+    const unsigned r = slot / spr, c = slot % spr;
+    return c < (unsigned)Ly::kCPR ? r * row_bytes + 16u * c : 0x7fffffffu;
+  }
+};
+
+// Buffer resource over the key rows of a tile of K or V for one head: the
+// record ends with the last row the tile may see, so loads of rows past
+// `count` (a span's ragged end) return 0 and never leave the tensor.
+constexpr int kRsrcWord3 = 0x00020000;
+
+template <int D>
+__device__ inline const char* tile_base(const void* base, const StepParams& p, const WorkItem& wi, const KTile& kt) {
+  return (const char*)base + (((long long)wi.b * p.Sk + kt.local0) * p.Hkv + wi.g) * (long long)(D * 2);
+}
+
+// Starts the copy of tile kt of K into kdst and of V into vdst.  Rows past
+// `count` load as 0: masked keys for K, zero-weighted values for V.
+template <int D>
+__device__ inline void stage_tile(const StepParams& p, const Lane<D>& ln, const WorkItem& wi, const KTile& kt,
+                                  RA_LDS char* kdst, RA_LDS char* vdst) {
+  typedef Layout<D> Ly;
+  const int nrec = (kt.count - 1) * (int)ln.row_bytes + 2 * D;
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)tile_base<D>(p.k, p, wi, kt), (short)0, nrec, kRsrcWord3);
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)tile_base<D>(p.v, p, wi, kt), (short)0, nrec, kRsrcWord3);
+#pragma unroll
+  for (int i = 0; i < Ly::kKDma / 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (RA_LDS void*)(kdst + (ln.wave * (Ly::kKDma / 4) + i) * 1024), 16,
+                                             (int)ln.kgo(i), 0, 0, 0);
+  // V: instruction ins goes to wave ins % 4
+#pragma unroll
+  for (int j = 0; j < (Ly::kVDma + 3) / 4; ++j) {
+    const int ins = 4 * j + ln.wave;
+    if (ins < Ly::kVDma)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (RA_LDS void*)(vdst + ins * 1024), 16, (int)ln.vgo(ins), 0, 0, 0);
+  }
+}
+
+__device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Iteration t.  PAR = t mod 2 names the LDS buffers statically: tile t is read
+// from kbuf[PAR] / vbuf[PAR]; tile t+1 is started first, into kbuf[PAR ^ 1] /
+// vbuf[PAR ^ 1].
+template <int D, int PAR>
+__device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const TilePlan& tp, const WorkItem& wi,
+                                 int t, RA_LDS char* const* kbuf, RA_LDS char* const* vbuf, int lane, int wave) {
+  typedef Layout<D> Ly;
+  const Lane<D> ln((unsigned)(p.Hkv * D * 2), wave);
+  const KTile ti = tp.tile(p, t);
+  const bool more = t + 1 < tp.n;
+  if (more) stage_tile<D>(p, ln, wi, tp.tile(p, t + 1), kbuf[PAR ^ 1], vbuf[PAR ^ 1]);
+
+  // S^T = K Q^T
+  const unsigned kb0 = ln.kb0();
+  f32x16 s[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) s[qb] = f32x16{};
+#pragma unroll
+  for (int u = 0; u < D / 16; ++u) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(kbuf[PAR], kb0 ^ (32u * u)));
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.q[qb][u], s[qb], 0, 0, 0);
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+  // mask (tiles past the unmasked ones only; a uniform branch): key k of
+  // the tile is visible to row q iff k < lim(q)
+  const int L = lane >> 5;
+  if (t >= tp.n_full) {
+    // rows of this wave see keys < (qglob0 - glob0 + 1) + row, clamped so the
+    // sum stays in int range (|row| < 256)
+    const long long d0 = wi.qglob0 - ti.glob0 + 1;
+    const int dc = p.causal ? (int)max(-1024LL, min(1024LL, d0)) : 1024;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int lim = min(ti.count, max(0, dc + 64 * wave + 32 * qb + (lane & 31)));
+      // key of register r is 16(r/8) + r%8 + 8L: compare the constant part
+      const int lim_l = lim - 8 * L;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (16 * (r >> 3) + (r & 7) >= lim_l) s[qb][r] = kNegInf;
+    }
+  }
+
+  // running maximum; rescale only when it grows by more than 2^kTau
+  bool grow[kQB];
+  bool any = false;
+  float m_new[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    float tmax = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[qb][r]);
+    tmax = max_halves(tmax);
+    m_new[qb] = fmaxf(ws.m_ref[qb], tmax);
+    // -inf reference: the difference is +inf and the maximum is taken;
+    // both -inf: NaN compares false and nothing moves.
+    grow[qb] = (m_new[qb] - ws.m_ref[qb]) * p.sl2 > kTau;
+    any |= grow[qb];
+  }
+  if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float alpha = grow[qb] ? __builtin_amdgcn_exp2f((ws.m_ref[qb] - m_new[qb]) * p.sl2) : 1.f;
+      if (grow[qb]) ws.m_ref[qb] = m_new[qb];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) ws.o[db][qb] *= alpha;
+      ws.l_part[qb] *= alpha;
+    }
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+  // P = exp2(S sl2 - m sl2), rounded to bf16 as the B operand of O^T += V^T P^T
+  bf16x8 pb[kQB][2];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const float mb = ws.m_ref[qb] == kNegInf ? 0.f : ws.m_ref[qb] * p.sl2;
+    float lsum = 0.f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * hf + e], p.sl2, -mb));
+        lsum += x[e];
+      }
+      pb[qb][hf] = __builtin_convertvector(x, bf16x8);
+      // one 8-key group at a time keeps the exponentials' temporaries few
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    ws.l_part[qb] += lsum;
+    // materialise the row sum here: otherwise the adds sink into the next
+    // tile and keep this tile's 32 probabilities alive across it
+    asm volatile("" : "+v"(ws.l_part[qb]));
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+  const unsigned vb0 = ln.vb0();
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const unsigned off = vb0 + 16 * hf * Ly::kVStride + 64 * db;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vbuf[PAR] + off));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vbuf[PAR] + off + 4 * Ly::kVStride));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+        ws.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][hf], ws.o[db][qb], 0, 0, 0);
+    }
+
+  wait_loads();
+  __syncthreads();
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_step_bf16_kernel(StepParams p) {
+  typedef Layout<D> Ly;
+  __shared__ __attribute__((aligned(16))) char k0_raw[Ly::kKTileBytes];
+  __shared__ __attribute__((aligned(16))) char k1_raw[Ly::kKTileBytes];
+  __shared__ __attribute__((aligned(16))) char v0_raw[Ly::kVTileBytes];
+  __shared__ __attribute__((aligned(16))) char v1_raw[Ly::kVTileBytes];
+  RA_LDS char* const kbuf[2] = {(RA_LDS char*)k0_raw, (RA_LDS char*)k1_raw};
+  RA_LDS char* const vbuf[2] = {(RA_LDS char*)v0_raw, (RA_LDS char*)v1_raw};
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  WorkItem wi;
+  if (!decode_work<kBQBf16>(p, wi)) return;
+  const TilePlan tp = plan_tiles(p, wi.qglob0, wi.qglob0 + wi.qrows - 1);
+  if (tp.n == 0) {
+    store_identity<D, kThreads>(p, wi);
+    return;
+  }
+
+  // prologue: tile 0 in flight while Q is read
+  {
+    const Lane<D> ln((unsigned)(p.Hkv * D * 2), wave);
+    stage_tile<D>(p, ln, wi, tp.tile(p, 0), kbuf[0], vbuf[0]);
+  }
+  WaveState<D> ws;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int wrow = 64 * wave + 32 * qb + (lane & 31);
+    const long long orow = ((long long)wi.b * p.Sq + wi.qlocal0 + wrow) * p.Hq + wi.h;  // (b, row, h)
+    const uint16_t* qrow = (const uint16_t*)p.q + orow * D;
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u)
+      ws.q[qb][u] = wrow < wi.qrows ? *(const bf16x8*)(qrow + 16 * u + 8 * (lane >> 5)) : bf16x8{};
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) ws.o[db][qb] = f32x16{};
+    ws.m_ref[qb] = kNegInf;
+    ws.l_part[qb] = 0.f;
+  }
+  wait_loads();
+  __syncthreads();
+
+  // main loop, unrolled by two so that buffers are named statically:
+  // iteration t uses parity t mod 2.
+  int t = 0;
+  for (; t + 1 < tp.n; t += 2) {
+    step_tile<D, 0>(ws, p, tp, wi, t, kbuf, vbuf, lane, wave);
+    step_tile<D, 1>(ws, p, tp, wi, t + 1, kbuf, vbuf, lane, wave);
+  }
+  if (t < tp.n) step_tile<D, 0>(ws, p, tp, wi, t, kbuf, vbuf, lane, wave);
+
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int wrow = 64 * wave + 32 * qb + (lane & 31);
+    const long long orow = ((long long)wi.b * p.Sq + wi.qlocal0 + wrow) * p.Hq + wi.h;
+    finish_rows<D, kQB>(p, ws.o, qb, ws.m_ref[qb], ws.l_part[qb], wrow < wi.qrows, orow, lane);
+  }
+}
+
+template <int D>
+hipError_t launch(const StepParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(attn_step_bf16_kernel<D>, dim3(8 * p.per_xcd), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_step_bf16(const StepParams& p, int D, hipStream_t s) {
+  if (D == 128) return launch<128>(p, s);
+  if (D == 64) return launch<64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ra

@@ -166,8 +166,9 @@ bool build_params(const ra_step_desc* d, const void* q, const void* k, const voi
   if (p->nqs == 0) return false;
   for (int i = p->nqs; i < 2; ++i) p->qs_start[i] = p->qs_len[i] = p->qs_off[i] = 0;
   for (int i = p->nks; i < 2; ++i) p->ks_start[i] = p->ks_len[i] = p->ks_off[i] = 0;
-  p->qt_span0 = (int)((p->qs_len[0] + ra::kBQ - 1) / ra::kBQ);
-  p->n_qtiles = p->qt_span0 + (int)((p->qs_len[1] + ra::kBQ - 1) / ra::kBQ);
+  const int bq = ra::step_rows(d->dtype);
+  p->qt_span0 = (int)((p->qs_len[0] + bq - 1) / bq);
+  p->n_qtiles = p->qt_span0 + (int)((p->qs_len[1] + bq - 1) / bq);
   p->n_work = p->B * p->Hq * p->n_qtiles;
   p->per_xcd = (p->n_work + 7) / 8;
   return true;

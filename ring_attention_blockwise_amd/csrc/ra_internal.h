@@ -6,9 +6,14 @@
 
 namespace ra {
 
-// Query rows per workgroup (4 waves x 32 rows) and keys per LDS tile.
+// Query rows per workgroup of the f32 kernel (4 waves x 32 rows) and of the
+// bf16 kernel (4 waves x 64 rows); keys per LDS tile of both.
 constexpr int kBQ = 128;
+constexpr int kBQBf16 = 256;
 constexpr int kBK = 32;
+
+// Query rows per workgroup for dtype 0 = f32, 1 = bf16.
+inline int step_rows(int dtype) { return dtype == 1 ? kBQBf16 : kBQ; }
 
 // Everything one launch of the attention step kernel needs.  Spans are the
 // (at most two) query / key spans of the step in local row order; only query
@@ -33,8 +38,11 @@ struct StepParams {
   int per_xcd;              // ceil(n_work / 8)
 };
 
-// dtype: 0 = f32, 1 = bf16; D in {64, 128}.
+// dtype: 0 = f32, 1 = bf16; D in {64, 128}.  The work decomposition of p
+// (n_qtiles, qt_span0) must use step_rows(dtype) rows per query tile.
 hipError_t launch_attn_step(const StepParams& p, int dtype, int D, hipStream_t s);
+hipError_t launch_attn_step_f32(const StepParams& p, int D, hipStream_t s);
+hipError_t launch_attn_step_bf16(const StepParams& p, int D, hipStream_t s);
 
 hipError_t launch_lse_merge(long long rows, int D, const float* o_a,
                             const float* lse_a, const float* o_b,
