@@ -61,25 +61,29 @@ struct KTile {
 };
 
 struct TilePlan {
-  int nf[2], nr[2];  // full and masked tiles per span
-  long long hi[2];   // keys of the span visible to the work item's last row
+  int nf[2], nr[2];    // full and masked tiles per span
+  long long hi[2];     // keys of the span visible to the work item's last row
+  long long off[2];    // first local row of each key span
+  long long start[2];  // its global position
   int n_full, n;
 
-  __device__ KTile tile(const StepParams& p, int t) const {
-    int s;
+  // Only selects between the two spans: no indexing by a run-time span
+  // number, which would re-read the kernel arguments on every tile.
+  __device__ KTile tile(int t) const {
+    bool s1;
     long long kin;
     if (t < n_full) {
-      s = t < nf[0] ? 0 : 1;
-      kin = (long long)(s ? t - nf[0] : t) * kBK;
+      s1 = t >= nf[0];
+      kin = (long long)(s1 ? t - nf[0] : t) * kBK;
     } else {
       const int u = t - n_full;
-      s = u < nr[0] ? 0 : 1;
-      kin = (long long)(nf[s] + (s ? u - nr[0] : u)) * kBK;
+      s1 = u >= nr[0];
+      kin = (long long)(s1 ? nf[1] + u - nr[0] : nf[0] + u) * kBK;
     }
     KTile kt;
-    kt.local0 = p.ks_off[s] + kin;
-    kt.glob0 = p.ks_start[s] + kin;
-    kt.count = (int)min((long long)kBK, hi[s] - kin);
+    kt.local0 = (s1 ? off[1] : off[0]) + kin;
+    kt.glob0 = (s1 ? start[1] : start[0]) + kin;
+    kt.count = (int)min((long long)kBK, (s1 ? hi[1] : hi[0]) - kin);
     return kt;
   }
 };
@@ -102,6 +106,8 @@ __device__ inline TilePlan plan_tiles(const StepParams& p, long long qglob0, lon
       full = max(full, 0LL);
     }
     tp.hi[s] = hi;
+    tp.off[s] = p.ks_off[s];
+    tp.start[s] = p.ks_start[s];
     tp.nf[s] = (int)(full / kBK);
     tp.nr[s] = (int)((hi - (long long)tp.nf[s] * kBK + kBK - 1) / kBK);
     tp.n_full += tp.nf[s];

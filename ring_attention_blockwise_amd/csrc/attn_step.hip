@@ -101,9 +101,9 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
                                  const WorkItem& wi, int t, RA_LDS char* const* kbuf, RA_LDS char* const* vbuf,
                                  long long qg, int lane) {
   typedef Layout<D> Ly;
-  const KTile ti = tp.tile(p, t);
+  const KTile ti = tp.tile(t);
   const bool more = t + 1 < tp.n;
-  if (more) st.load(p, wi, tp.tile(p, t + 1));
+  if (more) st.load(p, wi, tp.tile(t + 1));
 
   const int L = lane >> 5;
   f32x16 s = {};
@@ -196,7 +196,7 @@ void attn_step_f32_kernel(StepParams p) {
 
   TileStage<D> st;
   st.init(p);
-  st.load(p, wi, tp.tile(p, 0));
+  st.load(p, wi, tp.tile(0));
   WaveState<D> ws;
   {
     const float* qrow = (const float*)p.q + orow * D;

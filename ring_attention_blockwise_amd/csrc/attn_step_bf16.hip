@@ -23,7 +23,9 @@
 //     LDS bit, 16 bytes per lane), so staging takes no registers and no LDS
 //     store instructions.  Tile t+1 is started at the top of iteration t and
 //     waited for just before the barrier that ends it, so its latency hides
-//     behind a whole tile of work.
+//     behind a whole tile of work.  The per-tile bookkeeping (which rows the
+//     next tile holds, where they are) advances a small scalar cursor; the
+//     per-lane DMA offsets are computed once per work item.
 //   * Only key tiles with at least one visible key are visited; tiles all of
 //     whose keys every row of the work item sees run first and skip the mask.
 //
@@ -62,18 +64,18 @@ struct Layout {
   // in distinct banks.
   static constexpr int kKStride = kRowBytes;
   static constexpr int kKTileBytes = kBK * kKStride;
-  // V tile in LDS: 32 rows, padded by 64 bytes so that the 4 rows one
-  // transposing read touches per pass start 64 bytes apart modulo the 256
-  // bytes of the banks.
-  static constexpr int kVStride = kRowBytes + 64;
+  // V tile in LDS: 32 rows of 2D bytes; chunk c of row r sits at c ^ vsw(r),
+  // which puts the 4 rows one transposing read touches per pass (64 bytes
+  // each) in distinct banks.
+  static constexpr int kVStride = kRowBytes;
   static constexpr int kVTileBytes = kBK * kVStride;
-  // DMA: one instruction writes 64 consecutive 16-byte slots (1 KiB).
-  static constexpr int kKDma = kKTileBytes / 1024;
-  static constexpr int kVDma = kVTileBytes / 1024;
-  static_assert(kKTileBytes % 1024 == 0 && kVTileBytes % 1024 == 0, "whole DMA instructions");
-  static_assert(kKDma % 4 == 0, "K instructions split evenly over the 4 waves");
+  // DMA: one instruction writes 64 consecutive 16-byte slots (1 KiB); each
+  // wave copies kDma of them per tile for K and as many for V.
+  static constexpr int kDma = kKTileBytes / 1024 / 4;
+  static_assert(kKTileBytes % 4096 == 0, "K and V instructions split evenly over the 4 waves");
 
   __device__ static unsigned ksw(unsigned r) { return (kCPR == 16 ? r : r >> 1) & (kCPR - 1); }
+  __device__ static unsigned vsw(unsigned r) { return (4u * ((r & 3u) >> (kCPR == 16 ? 0 : 1))) & (kCPR - 1); }
 };
 
 __device__ inline unsigned sigma(unsigned i) { return (i & ~12u) | ((i & 4u) << 1) | ((i & 8u) >> 1); }
@@ -106,28 +108,68 @@ struct Lane {
     return (rho * Ly::kKStride) | (16u * (Ly::ksw(rho) ^ (lane >> 5)));
   }
   // Transposing V reads.  In each 16-lane group g (lanes 16g + s) lane s
-  // addresses key row 8(g/2) + s/4 (+16h for key half h, +4 for the second
-  // read) at column d = 32db + 16(g%2) + 4(s%4); the read hands lane s
+  // addresses key row r = 8(g/2) + s/4 (+16h for key half h, +4 for the
+  // second read) at column d = 32db + 16(g%2) + 4(s%4); the read hands lane s
   // element s%4 of the chunk of lane 4j + s/4 as its element j, i.e. column
   // 32db + 16(g%2) + s of key rows +j: the A operand of the PV MFMA.
+  // r mod 4 = s/4 whatever h, so vsw(r) is fixed per lane and the address of
+  // block db is vb0() ^ 64 db plus a whole number of rows.
   __device__ unsigned vb0() const {
     const unsigned g = lane >> 4, s = lane & 15u;
-    return (8u * (g >> 1) + (s >> 2)) * Ly::kVStride + 2u * (16u * (g & 1u) + 4u * (s & 3u));
+    const unsigned r = 8u * (g >> 1) + (s >> 2);
+    const unsigned x = 2u * (g & 1u) + ((s & 3u) >> 1);  // chunk of d within block 0
+    return r * Ly::kVStride + 16u * (x ^ Ly::vsw(r)) + 2u * (4u * (s & 1u));
   }
-  // Tile offsets of the chunks this lane copies.  K slot s holds row
-  // s / kCPR, chunk (s % kCPR) ^ ksw(row).  V slot s holds row s / (kVStride
-  // / 16), chunk s % (kVStride / 16); chunks past kCPR are padding and load
-  // from past the record (zeros).
-  __device__ unsigned kgo(int i) const {
-    const unsigned slot = (wave * (Ly::kKDma / 4) + i) * 64 + lane;
+  // Tile offset of the chunk this lane copies with DMA instruction i: slot s
+  // of a tile holds row s / kCPR, chunk (s % kCPR) ^ sw(row).
+  __device__ unsigned dma_offset(int i, bool v) const {
+    const unsigned slot = (wave * Ly::kDma + i) * 64 + lane;
     const unsigned r = slot / Ly::kCPR;
-    return r * row_bytes + 16u * ((slot % Ly::kCPR) ^ Ly::ksw(r));
+    return r * row_bytes + 16u * ((slot % Ly::kCPR) ^ (v ? Ly::vsw(r) : Ly::ksw(r)));
   }
-  __device__ unsigned vgo(int ins) const {
-    constexpr unsigned spr = Ly::kVStride / 16;
-    const unsigned slot = ins * 64 + lane;
-    const unsigned r = slot / spr, c = slot % spr;
-    return c < (unsigned)Ly::kCPR ? r * row_bytes + 16u * c : 0x7fffffffu;
+};
+
+// Walks the key tiles of a work item in the order the tile plan fixes (the
+// unmasked tiles of each span, then the masked ones), one scalar update per
+// tile; only the first tile of a segment recomputes from the plan.
+struct TileCursor {
+  long long local0, glob0;  // first local row of the tile, its global position
+  long long vis;            // rows of the span visible from local0 on
+  int rem;                  // tiles left in the segment, this one included
+  int seg;                  // 0, 1: unmasked tiles of span 0, 1; 2, 3: masked
+
+  __device__ int count() const { return (int)min((long long)kBK, vis); }
+  __device__ bool masked() const { return seg >= 2; }
+
+  __device__ bool enter(const TilePlan& tp, int j) {
+    // selects only: a run-time index into the plan's arrays would put the
+    // plan in scratch memory
+    const bool s = j & 1;
+    const int nf = s ? tp.nf[1] : tp.nf[0];
+    const int n = j < 2 ? nf : (s ? tp.nr[1] : tp.nr[0]);
+    if (n == 0) return false;
+    const long long kin = j < 2 ? 0 : (long long)nf * kBK;
+    local0 = (s ? tp.off[1] : tp.off[0]) + kin;
+    glob0 = (s ? tp.start[1] : tp.start[0]) + kin;
+    vis = (s ? tp.hi[1] : tp.hi[0]) - kin;
+    rem = n;
+    seg = j;
+    return true;
+  }
+  __device__ void first(const TilePlan& tp) {
+    for (int j = 0; j < 4; ++j)
+      if (enter(tp, j)) return;
+  }
+  __device__ void advance(const TilePlan& tp) {
+    if (rem > 1) {
+      --rem;
+      local0 += kBK;
+      glob0 += kBK;
+      vis -= kBK;
+      return;
+    }
+    for (int j = seg + 1; j < 4; ++j)
+      if (enter(tp, j)) return;
   }
 };
 
@@ -136,32 +178,45 @@ struct Lane {
 // `count` (a span's ragged end) return 0 and never leave the tensor.
 constexpr int kRsrcWord3 = 0x00020000;
 
+// DMA staging of K and V tiles for one work item.
 template <int D>
-__device__ inline const char* tile_base(const void* base, const StepParams& p, const WorkItem& wi, const KTile& kt) {
-  return (const char*)base + (((long long)wi.b * p.Sk + kt.local0) * p.Hkv + wi.g) * (long long)(D * 2);
-}
-
-// Starts the copy of tile kt of K into kdst and of V into vdst.  Rows past
-// `count` load as 0: masked keys for K, zero-weighted values for V.
-template <int D>
-__device__ inline void stage_tile(const StepParams& p, const Lane<D>& ln, const WorkItem& wi, const KTile& kt,
-                                  RA_LDS char* kdst, RA_LDS char* vdst) {
+struct Stager {
   typedef Layout<D> Ly;
-  const int nrec = (kt.count - 1) * (int)ln.row_bytes + 2 * D;
-  const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)tile_base<D>(p.k, p, wi, kt), (short)0, nrec, kRsrcWord3);
-  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)tile_base<D>(p.v, p, wi, kt), (short)0, nrec, kRsrcWord3);
+  const char* khead;   // row 0 of this (batch, kv head) in K
+  const char* vhead;
+  unsigned row_bytes;
+  unsigned ko[Ly::kDma], vo[Ly::kDma];  // this lane's chunk offsets in a tile
+  int wave;
+
+  __device__ void init(const StepParams& p, const WorkItem& wi, const Lane<D>& ln) {
+    row_bytes = ln.row_bytes;
+    const long long head = ((long long)wi.b * p.Sk * p.Hkv + wi.g) * (long long)(D * 2);
+    khead = (const char*)p.k + head;
+    vhead = (const char*)p.v + head;
+    wave = ln.wave;
 #pragma unroll
-  for (int i = 0; i < Ly::kKDma / 4; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (RA_LDS void*)(kdst + (ln.wave * (Ly::kKDma / 4) + i) * 1024), 16,
-                                             (int)ln.kgo(i), 0, 0, 0);
-  // V: instruction ins goes to wave ins % 4
-#pragma unroll
-  for (int j = 0; j < (Ly::kVDma + 3) / 4; ++j) {
-    const int ins = 4 * j + ln.wave;
-    if (ins < Ly::kVDma)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (RA_LDS void*)(vdst + ins * 1024), 16, (int)ln.vgo(ins), 0, 0, 0);
+    for (int i = 0; i < Ly::kDma; ++i) {
+      ko[i] = ln.dma_offset(i, false);
+      vo[i] = ln.dma_offset(i, true);
+    }
   }
-}
+
+  // Starts the copy of the tile at cursor c into kdst / vdst.  Rows past
+  // `count` load as 0: masked keys for K, zero-weighted values for V.
+  __device__ void issue(const TileCursor& c, RA_LDS char* kdst, RA_LDS char* vdst) const {
+    const long long off = c.local0 * (long long)row_bytes;
+    const int nrec = (c.count() - 1) * (int)row_bytes + 2 * D;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(khead + off), (short)0, nrec, kRsrcWord3);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vhead + off), (short)0, nrec, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < Ly::kDma; ++i) {
+      RA_LDS char* kd = kdst + (wave * Ly::kDma + i) * 1024;
+      RA_LDS char* vd = vdst + (wave * Ly::kDma + i) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (RA_LDS void*)kd, 16, (int)ko[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (RA_LDS void*)vd, 16, (int)vo[i], 0, 0, 0);
+    }
+  }
+};
 
 __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -170,12 +225,14 @@ __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "mem
 // vbuf[PAR ^ 1].
 template <int D, int PAR>
 __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const TilePlan& tp, const WorkItem& wi,
-                                 int t, RA_LDS char* const* kbuf, RA_LDS char* const* vbuf, int lane, int wave) {
-  typedef Layout<D> Ly;
+                                 const Stager<D>& st, TileCursor& cur, int t, RA_LDS char* const* kbuf,
+                                 RA_LDS char* const* vbuf, int lane, int wave) {
   const Lane<D> ln((unsigned)(p.Hkv * D * 2), wave);
-  const KTile ti = tp.tile(p, t);
-  const bool more = t + 1 < tp.n;
-  if (more) stage_tile<D>(p, ln, wi, tp.tile(p, t + 1), kbuf[PAR ^ 1], vbuf[PAR ^ 1]);
+  const TileCursor ti = cur;
+  if (t + 1 < tp.n) {
+    cur.advance(tp);
+    st.issue(cur, kbuf[PAR ^ 1], vbuf[PAR ^ 1]);
+  }
 
   // S^T = K Q^T
   const unsigned kb0 = ln.kb0();
@@ -193,14 +250,14 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
   // mask (tiles past the unmasked ones only; a uniform branch): key k of
   // the tile is visible to row q iff k < lim(q)
   const int L = lane >> 5;
-  if (t >= tp.n_full) {
+  if (ti.masked()) {
     // rows of this wave see keys < (qglob0 - glob0 + 1) + row, clamped so the
     // sum stays in int range (|row| < 256)
     const long long d0 = wi.qglob0 - ti.glob0 + 1;
     const int dc = p.causal ? (int)max(-1024LL, min(1024LL, d0)) : 1024;
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
-      const int lim = min(ti.count, max(0, dc + 64 * wave + 32 * qb + (lane & 31)));
+      const int lim = min(ti.count(), max(0, dc + 64 * wave + 32 * qb + (lane & 31)));
       // key of register r is 16(r/8) + r%8 + 8L: compare the constant part
       const int lim_l = lim - 8 * L;
 #pragma unroll
@@ -267,9 +324,9 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const unsigned off = vb0 + 16 * hf * Ly::kVStride + 64 * db;
+      const unsigned off = (vb0 ^ (64u * db)) + 16 * hf * Layout<D>::kVStride;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vbuf[PAR] + off));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vbuf[PAR] + off + 4 * Ly::kVStride));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vbuf[PAR] + off + 4 * Layout<D>::kVStride));
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb)
@@ -303,10 +360,11 @@ void attn_step_bf16_kernel(StepParams p) {
   }
 
   // prologue: tile 0 in flight while Q is read
-  {
-    const Lane<D> ln((unsigned)(p.Hkv * D * 2), wave);
-    stage_tile<D>(p, ln, wi, tp.tile(p, 0), kbuf[0], vbuf[0]);
-  }
+  Stager<D> st;
+  st.init(p, wi, Lane<D>((unsigned)(p.Hkv * D * 2), wave));
+  TileCursor cur;
+  cur.first(tp);
+  st.issue(cur, kbuf[0], vbuf[0]);
   WaveState<D> ws;
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
@@ -328,10 +386,10 @@ void attn_step_bf16_kernel(StepParams p) {
   // iteration t uses parity t mod 2.
   int t = 0;
   for (; t + 1 < tp.n; t += 2) {
-    step_tile<D, 0>(ws, p, tp, wi, t, kbuf, vbuf, lane, wave);
-    step_tile<D, 1>(ws, p, tp, wi, t + 1, kbuf, vbuf, lane, wave);
+    step_tile<D, 0>(ws, p, tp, wi, st, cur, t, kbuf, vbuf, lane, wave);
+    step_tile<D, 1>(ws, p, tp, wi, st, cur, t + 1, kbuf, vbuf, lane, wave);
   }
-  if (t < tp.n) step_tile<D, 0>(ws, p, tp, wi, t, kbuf, vbuf, lane, wave);
+  if (t < tp.n) step_tile<D, 0>(ws, p, tp, wi, st, cur, t, kbuf, vbuf, lane, wave);
 
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
