@@ -52,7 +52,7 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kQB = 2;         // 32-row query blocks per wave
-static_assert(kBQBf16 == 4 * 32 * kQB, "workgroup rows");
+constexpr int kBQBf16 = 4 * 32 * kQB;  // workgroup rows
 static_assert(kBK == 32, "one 32x32 score block per query block and tile");
 
 template <int D>
@@ -245,6 +245,13 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.q[qb][u], s[qb], 0, 0, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int u = 2; u < D / 16; ++u) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
   __builtin_amdgcn_sched_barrier(0);
   // mask (tiles past the unmasked ones only; a uniform branch): key k of
@@ -258,11 +265,18 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       const int lim = min(ti.count(), max(0, dc + 64 * wave + 32 * qb + (lane & 31)));
-      // key of register r is 16(r/8) + r%8 + 8L: compare the constant part
-      const int lim_l = lim - 8 * L;
+      // key of register r is 16(r/8) + r%8 + 8L: it is visible iff
+      // lim - 8L - 1 - (16(r/8) + r%8) >= 0.  The sign bit of that difference
+      // selects -inf with a bitfield insert (no compare masks, which would
+      // take scalar registers).
+      const int lim_l = lim - 8 * L - 1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (16 * (r >> 3) + (r & 7) >= lim_l) s[qb][r] = kNegInf;
+      for (int r = 0; r < 16; ++r) {
+        int d = lim_l - (16 * (r >> 3) + (r & 7));
+        asm volatile("" : "+v"(d));
+        const unsigned m = (unsigned)(d >> 31);
+        s[qb][r] = __uint_as_float((m & 0xff800000u) | (~m & __float_as_uint(s[qb][r])));
+      }
     }
   }
 
@@ -332,6 +346,13 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
       for (int qb = 0; qb < kQB; ++qb)
         ws.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][hf], ws.o[db][qb], 0, 0, 0);
     }
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+  for (int i = 2; i < 2 * (D / 32); ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
 
   wait_loads();
   __syncthreads();
@@ -406,6 +427,8 @@ hipError_t launch(const StepParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+int attn_step_rows_bf16() { return kBQBf16; }
 
 hipError_t launch_attn_step_bf16(const StepParams& p, int D, hipStream_t s) {
   if (D == 128) return launch<128>(p, s);

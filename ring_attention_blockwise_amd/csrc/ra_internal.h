@@ -6,14 +6,16 @@
 
 namespace ra {
 
-// Query rows per workgroup of the f32 kernel (4 waves x 32 rows) and of the
-// bf16 kernel (4 waves x 64 rows); keys per LDS tile of both.
+// Query rows per workgroup of the f32 kernel (4 waves x 32 rows); keys per
+// LDS tile of both kernels.  The bf16 kernel states its own workgroup rows.
 constexpr int kBQ = 128;
-constexpr int kBQBf16 = 256;
 constexpr int kBK = 32;
 
+// Query rows per workgroup of the bf16 kernel (defined with it).
+int attn_step_rows_bf16();
+
 // Query rows per workgroup for dtype 0 = f32, 1 = bf16.
-inline int step_rows(int dtype) { return dtype == 1 ? kBQBf16 : kBQ; }
+inline int step_rows(int dtype) { return dtype == 1 ? attn_step_rows_bf16() : kBQ; }
 
 // Everything one launch of the attention step kernel needs.  Spans are the
 // (at most two) query / key spans of the step in local row order; only query
