@@ -32,8 +32,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 METRIC = "attention TFLOPS per rank-share (1 GPU) and % of bf16 MFMA peak"
-KERNEL_SOURCES = ["ring_attention_blockwise_amd/csrc/attn_step.hip",
+KERNEL_SOURCES = ["ring_attention_blockwise_amd/csrc/attn_step_bf16.hip",
+                  "ring_attention_blockwise_amd/csrc/attn_common.h",
                   "ring_attention_blockwise_amd/csrc/ra_internal.h"]
+KERNEL_NAME = "attn_step_bf16_kernel<128>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_step_traffic.json")
 
 
@@ -296,7 +298,7 @@ def main():
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(name), "kernel": "attn_step_kernel<Bf16<128>>",
+                     "traffic": measured_traffic(name), "kernel": KERNEL_NAME,
                      "launches_per_step": nl, "avg_launch_us": round(launch_us, 2)},
         "cpu_baseline": cpu,
         "aux": aux,
