@@ -229,6 +229,15 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
                                  RA_LDS char* const* vbuf, int lane, int wave) {
   const Lane<D> ln((unsigned)(p.Hkv * D * 2), wave);
   const TileCursor ti = cur;
+  // Two workgroups share each CU; the wave arbiter favours the older one,
+  // which then finishes its (equal) work long before the younger.  Swapping
+  // the issue priority every 32 tiles, in opposite phase for the first and
+  // second workgroup a CU receives (dispatch fills one slot on each of the
+  // 256 CUs before the second), lets both progress at about the same rate.
+  if ((((unsigned)t >> 5) ^ (blockIdx.x >> 8)) & 1u)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
   if (t + 1 < tp.n) {
     cur.advance(tp);
     st.issue(cur, kbuf[PAR ^ 1], vbuf[PAR ^ 1]);
