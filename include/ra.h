@@ -157,6 +157,22 @@ int ra_rank_forward(const ra_rank_desc* d, const void* q_local,
                     float* lse, void* stream);
 
 /*
+ * ra_allgather_forward -- the all-gather form of the same rank's attention:
+ * every key/value token is resident at once, so the rank's queries attend to
+ * the whole sequence in one launch with no per-step merge (ringmaster
+ * "Status", Ring row: the allgather rotater, the faster option that keeps
+ * all of K/V resident, beside the memory-optimal p2p ring).
+ *   q_local  [B, S/P, Hq, D]       this rank's queries in its local order
+ *   k_global [B, S, Hkv, D]        all keys in global token order; v_global same
+ *   o        [B, S/P, Hq, D] float32, lse [B, S/P, Hq] float32 (written, INIT)
+ * The result equals ra_rank_forward's (same definition; the order of the
+ * floating-point sums differs).  Requirements as for ra_rank_forward.
+ */
+int ra_allgather_forward(const ra_rank_desc* d, const void* q_local,
+                         const void* k_global, const void* v_global, float* o,
+                         float* lse, void* stream);
+
+/*
  * ra_ulysses_relayout -- the local pack/unpack around the Ulysses all-to-all
  * ("Sequence Parallelism II: DeepSpeed Ulysses and All-to-All Attention": a
  * rank goes from all heads of its tokens to all tokens of a subset of heads).

@@ -5,7 +5,7 @@ The functions here carry the C ABI's names and only marshal arguments: they
 check tensor devices, dtypes, shapes and contiguity, pass raw pointers and the
 current HIP stream, and raise ``RaError`` on a non-zero status.  Every step of
 the computation runs in the library's HIP kernels.  If libra.so is missing the
-import fails; build it with ``python -m ring_attention_blockwise_amd.build``.
+import fails; build it with ``python ring_attention_blockwise_amd/build.py``.
 
 Layouts (see include/ra.h): q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D] in float32
 or bfloat16; o [B, Sq, Hq, D] float32; lse [B, Sq, Hq] float32 (natural log).
@@ -62,7 +62,7 @@ class ra_plan_out(ctypes.Structure):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m ring_attention_blockwise_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python ring_attention_blockwise_amd/build.py`")
 # The library must share PyTorch's HIP runtime: torch hands it device pointers
 # and stream handles.  Both runtimes carry the soname libamdhip64.so.7, so
 # loading torch first makes the dynamic loader bind libra.so to torch's copy
@@ -77,16 +77,17 @@ _vp, _i32, _i64, _u32, _fp = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ct
 lib.ra_step.argtypes = [ctypes.POINTER(ra_step_desc), _vp, _vp, _vp, _fp, _fp, _u32, _vp]
 lib.ra_lse_merge.argtypes = [_i64, _i32, _fp, _fp, _fp, _fp, _fp, _fp, _vp]
 lib.ra_rank_forward.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp, _fp, _fp, _vp]
+lib.ra_allgather_forward.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp, _fp, _fp, _vp]
 lib.ra_ulysses_relayout.argtypes = [_i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp]
 lib.ra_plan.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ra_plan_out)]
 lib.ra_last_error.restype = ctypes.c_char_p
 lib.ra_last_error.argtypes = []
 lib.ra_abi_version.restype = ctypes.c_int
 lib.ra_abi_version.argtypes = []
-for _f in ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_ulysses_relayout", "ra_plan"):
+for _f in ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_allgather_forward", "ra_ulysses_relayout", "ra_plan"):
     getattr(lib, _f).restype = ctypes.c_int
 
-EXPORTS = ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_ulysses_relayout", "ra_plan",
+EXPORTS = ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_allgather_forward", "ra_ulysses_relayout", "ra_plan",
            "ra_last_error", "ra_abi_version")
 
 
@@ -208,6 +209,31 @@ def ra_rank_forward(q_local, k_shards, v_shards, o, lse, *, S: int, P: int, rank
                      1 if causal else 0, float(scale if scale is not None else D ** -0.5))
     _check(lib.ra_rank_forward(ctypes.byref(d), _ptr(q_local), _ptr(k_shards), _ptr(v_shards),
                                _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def ra_allgather_forward(q_local, k_global, v_global, o, lse, *, S: int, P: int, rank: int, order: str,
+                         causal: bool, scale: float | None = None, stream=None) -> None:
+    """Rank ``rank``'s attention over the whole sequence in one launch.
+    q_local [B, S/P, Hq, D]; k_global, v_global [B, S, Hkv, D] in global token
+    order; o and lse are written."""
+    torch = _torch()
+    _require(q_local, "q_local", ndim=4)
+    _require(k_global, "k_global", dtype=q_local.dtype, ndim=4)
+    _require(v_global, "v_global", dtype=q_local.dtype, ndim=4)
+    _require(o, "o", dtype=torch.float32, ndim=4)
+    _require(lse, "lse", dtype=torch.float32, ndim=3)
+    B, s_loc, Hq, D = q_local.shape
+    Hkv = k_global.shape[2]
+    if P * s_loc != S:
+        raise ValueError("q_local must hold S/P rows")
+    if tuple(k_global.shape) != (B, S, Hkv, D) or k_global.shape != v_global.shape:
+        raise ValueError("k_global and v_global must be [B, S, Hkv, D]")
+    if tuple(o.shape) != (B, s_loc, Hq, D) or tuple(lse.shape) != (B, s_loc, Hq):
+        raise ValueError("o must be [B, S/P, Hq, D] and lse [B, S/P, Hq]")
+    d = ra_rank_desc(_dtype_code(q_local), B, Hq, Hkv, D, S, P, rank, ORDERS[order],
+                     1 if causal else 0, float(scale if scale is not None else D ** -0.5))
+    _check(lib.ra_allgather_forward(ctypes.byref(d), _ptr(q_local), _ptr(k_global), _ptr(v_global),
+                                    _ptr(o), _ptr(lse), _stream(stream)))
 
 
 def ra_lse_merge(o_a, lse_a, o_b, lse_b, o_out, lse_out, *, stream=None) -> None:

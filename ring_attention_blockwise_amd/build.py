@@ -1,6 +1,6 @@
 """Build libra.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m ring_attention_blockwise_amd.build
+    python ring_attention_blockwise_amd/build.py
 
 Each source is compiled with hipcc to an object in ``_build/``, in parallel,
 then linked into ``ring_attention_blockwise_amd/libra.so``.

@@ -304,6 +304,36 @@ int ra_rank_forward(const ra_rank_desc* d, const void* q_local, const void* k_sh
   return ok();
 }
 
+int ra_allgather_forward(const ra_rank_desc* d, const void* q_local, const void* k_global, const void* v_global,
+                         float* o, float* lse, void* stream) {
+  if (!d) return fail(RA_E_INVAL, "descriptor is NULL");
+  int rc = check_ring(d->order, d->S, d->P, d->rank);
+  if (rc) return rc;
+  ra_step_desc sd;
+  sd.dtype = d->dtype;
+  sd.B = d->B;
+  sd.Hq = d->Hq;
+  sd.Hkv = d->Hkv;
+  sd.D = d->D;
+  sd.Sq = d->S / d->P;
+  sd.Sk = d->S;
+  sd.causal = d->causal;
+  sd.scale = d->scale;
+  const Spans qs = rank_spans(d->order, d->S, d->P, d->rank);
+  sd.n_qspans = qs.n;
+  for (int i = 0; i < 2; ++i) sd.qspans[i] = i < qs.n ? qs.s[i] : ra_span{0, 0};
+  sd.n_kspans = 1;
+  sd.kspans[0] = ra_span{0, d->S};
+  sd.kspans[1] = ra_span{0, 0};
+  rc = check_step(&sd, q_local, k_global, v_global, o, lse, RA_STEP_INIT);
+  if (rc) return rc;
+  ra::StepParams p;
+  if (!build_params(&sd, q_local, k_global, v_global, o, lse, false, &p)) return ok();
+  rc = launch_step(p, d->dtype, d->D, stream);
+  if (rc) return rc;
+  return ok();
+}
+
 int ra_lse_merge(int64_t rows, int32_t D, const float* o_a, const float* lse_a, const float* o_b,
                  const float* lse_b, float* o_out, float* lse_out, void* stream) {
   if (rows < 0) return fail(RA_E_INVAL, "rows must be >= 0");

@@ -83,13 +83,15 @@ def test_empty_step_enqueues_nothing():
     (dict(Hq=5), ra.RA_E_INVAL),
     (dict(D=80), ra.RA_E_UNSUPPORTED),
 ])
-def test_rank_forward_rejects_bad_descriptors(fields, status):
+@pytest.mark.parametrize("entry", ["ra_rank_forward", "ra_allgather_forward"])
+def test_rank_forward_rejects_bad_descriptors(fields, status, entry):
     f = dict(dtype=1, B=1, Hq=8, Hkv=2, D=128, S=4096, P=8, rank=0, order=1, causal=1, scale=0.088)
     f.update(fields)
     d = ra.ra_rank_desc(*[f[k] for k in ("dtype", "B", "Hq", "Hkv", "D", "S", "P", "rank", "order",
                                          "causal", "scale")])
-    assert ra.lib.ra_rank_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
+    assert getattr(ra.lib, entry)(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
     assert ra.ra_last_error()
+    assert getattr(ra.lib, entry)(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ra.RA_E_INVAL
 
 
 def test_merge_and_relayout_validation():
