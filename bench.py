@@ -140,6 +140,41 @@ def time_attention(ra, w, rank, steps, warmup):
     return wall, per, ok
 
 
+def time_allgather(ra, w, rank, ring_ms, reps=5):
+    """The all-gather form of the same rank's work: one launch over the whole
+    resident sequence, no per-step merge.  Against the ring it shows what the
+    per-step launches and fused merges cost."""
+    import torch
+    import seeded_inputs as si
+    q = to_device(si.tokens(w.seed_id, si.TENSOR_Q, w.B, w.S, w.Hq, w.D,
+                            ra.rank_spans(w.order, w.S, w.P, rank), w.dtype), w.dtype)
+    kg = to_device(si.tokens(w.seed_id, si.TENSOR_K, w.B, w.S, w.Hkv, w.D, [(0, w.S)], w.dtype,
+                             scale=w.k_scale), w.dtype)
+    vg = to_device(si.tokens(w.seed_id, si.TENSOR_V, w.B, w.S, w.Hkv, w.D, [(0, w.S)], w.dtype), w.dtype)
+    o = torch.empty((w.B, w.S // w.P, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.S // w.P, w.Hq), dtype=torch.float32, device="cuda")
+
+    def run():
+        ra.ra_allgather_forward(q, kg, vg, o, lse, S=w.S, P=w.P, rank=rank, order=w.order,
+                                causal=w.causal, scale=w.scale)
+
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = algorithmic_flops(w, rank)
+    del q, kg, vg, o, lse
+    torch.cuda.empty_cache()
+    return {"kernel": "allgather_forward", "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "frac_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "ring_ms": ring_ms,
+            "ring_over_allgather": ring_ms / ms}
+
+
 def time_merge(ra, rows, D, reps=20):
     """Standalone merge, rotating buffer sets so the working set exceeds the
     256 MB Infinity Cache."""
@@ -271,10 +306,15 @@ def main():
           f"{nl} launches of {launch_us:.1f} us", file=sys.stderr, flush=True)
     aux = []
     if not args.no_aux:
+        aux.append(time_allgather(ra, w, rank, ms))
         aux.append(time_merge(ra, w.B * (w.S // w.P) * w.Hq, w.D))
         aux.append(time_relayout(ra, 2, 8192, 16, 128, 8))
         for a in aux:
-            print(f"[bench] {a['kernel']}: {a['us']:.1f} us, {a['GB/s']:.0f} GB/s", file=sys.stderr, flush=True)
+            if "GB/s" in a:
+                print(f"[bench] {a['kernel']}: {a['us']:.1f} us, {a['GB/s']:.0f} GB/s", file=sys.stderr, flush=True)
+            else:
+                print(f"[bench] {a['kernel']}: {a['ms']:.3f} ms, {a['TFLOP/s']:.1f} TFLOP/s", file=sys.stderr,
+                      flush=True)
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)

@@ -95,6 +95,22 @@ class RankCase:
         torch.cuda.synchronize()
         return o.cpu().numpy(), lse.cpu().numpy()
 
+    def run_allgather(self, ra, rank, poison=True):
+        """ra_allgather_forward of ``rank``: the global K and V resident at once."""
+        import torch
+        q = to_device(self.q_rows(ra.rank_spans(self.order, self.S, self.P, rank)), self.dtype)
+        kg, vg = to_device(self.Kg, self.dtype), to_device(self.Vg, self.dtype)
+        s_loc = self.S // self.P
+        o = torch.empty(self.B, s_loc, self.Hq, self.D, device="cuda", dtype=torch.float32)
+        lse = torch.empty(self.B, s_loc, self.Hq, device="cuda", dtype=torch.float32)
+        if poison:
+            o.fill_(float("nan"))
+            lse.fill_(float("nan"))
+        ra.ra_allgather_forward(q, kg, vg, o, lse, S=self.S, P=self.P, rank=rank, order=self.order,
+                                causal=self.causal, scale=self.scale)
+        torch.cuda.synchronize()
+        return o.cpu().numpy(), lse.cpu().numpy()
+
     def reference(self, rank, rows=None):
         """Oracle (definition over the concatenated sequence), float64, for the
         rank's local rows ``rows`` (all rows if None)."""
