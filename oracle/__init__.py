@@ -16,6 +16,9 @@ Modules
                 definition), per-block partials, the log-sum-exp merge and the
                 oracle's own ring decomposition (used as an invariant only).
 ``relayout``    the Ulysses sequence<->head regrouping.
+``attention_backward``  dQ, dK, dV of the definition (the backward pass),
+                pinned by ``tests/test_oracle_backward.py`` against finite
+                differences of the forward definition.
 
 Every function cites the passage of the source pages it follows: the ringmaster
 package description (sections "Why", "Status", "Layout"), the blog posts
