@@ -173,6 +173,37 @@ int ra_allgather_forward(const ra_rank_desc* d, const void* q_local,
                          float* lse, void* stream);
 
 /*
+ * ra_rank_backward -- the backward pass of rank `rank`'s ring attention,
+ * simulated on one GPU: the flash-style reverse ring of ringmaster's
+ * description ("Status", Ring row, forward and backward; the note on the p2p
+ * and allgather paths).  dQ of the rank's rows accumulates locally over the P
+ * steps; the contribution to dK and dV of the block held at step s is added
+ * into that block's gradient (which in a real ring travels back to its owner
+ * with the block).  The arithmetic is the chain rule through the softmax:
+ *   P = exp(scale q K^T - L),  dP = dO V^T,  delta = rowsum(dO * O),
+ *   dS = P * (dP - delta),  dQ = scale dS K,  dK += scale dS^T Q,  dV += P^T dO,
+ * with L and O the forward's final log-sum-exp and output.
+ *   q_local   [B, S/P, Hq, D]        bf16, this rank's queries (local order)
+ *   k_shards, v_shards [P, B, S/P, Hkv, D]  bf16, as for ra_rank_forward
+ *   o         [B, S/P, Hq, D] float32, lse [B, S/P, Hq] float32 (ra_rank_forward's)
+ *   dout      [B, S/P, Hq, D]        bf16, the loss gradient of o
+ *   dq        [B, S/P, Hq, D] float32: written
+ *   dk_shards, dv_shards [P, B, S/P, Hkv, D] float32: ADDED to (the caller
+ *             zeroes them; running every rank into the same buffers gives the
+ *             full gradients)
+ *   delta     [B, S/P, Hq] float32: caller-provided workspace, written with
+ *             rowsum(dout * o)
+ * Built for bf16 with D = 128 (RA_E_UNSUPPORTED otherwise); other
+ * requirements as for ra_rank_forward.  Work is enqueued on `stream`: per
+ * launched step one dQ kernel, then one dK/dV kernel.
+ */
+int ra_rank_backward(const ra_rank_desc* d, const void* q_local,
+                     const void* k_shards, const void* v_shards,
+                     const float* o, const float* lse, const void* dout,
+                     float* dq, float* dk_shards, float* dv_shards,
+                     float* delta, void* stream);
+
+/*
  * ra_ulysses_relayout -- the local pack/unpack around the Ulysses all-to-all
  * ("Sequence Parallelism II: DeepSpeed Ulysses and All-to-All Attention": a
  * rank goes from all heads of its tokens to all tokens of a subset of heads).

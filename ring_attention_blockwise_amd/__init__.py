@@ -78,16 +78,20 @@ lib.ra_step.argtypes = [ctypes.POINTER(ra_step_desc), _vp, _vp, _vp, _fp, _fp, _
 lib.ra_lse_merge.argtypes = [_i64, _i32, _fp, _fp, _fp, _fp, _fp, _fp, _vp]
 lib.ra_rank_forward.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp, _fp, _fp, _vp]
 lib.ra_allgather_forward.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp, _fp, _fp, _vp]
+lib.ra_rank_backward.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp, _fp, _fp, _vp, _fp, _fp, _fp,
+                                 _fp, _vp]
 lib.ra_ulysses_relayout.argtypes = [_i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp]
 lib.ra_plan.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ra_plan_out)]
 lib.ra_last_error.restype = ctypes.c_char_p
 lib.ra_last_error.argtypes = []
 lib.ra_abi_version.restype = ctypes.c_int
 lib.ra_abi_version.argtypes = []
-for _f in ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_allgather_forward", "ra_ulysses_relayout", "ra_plan"):
+for _f in ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_allgather_forward", "ra_rank_backward",
+           "ra_ulysses_relayout", "ra_plan"):
     getattr(lib, _f).restype = ctypes.c_int
 
-EXPORTS = ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_allgather_forward", "ra_ulysses_relayout", "ra_plan",
+EXPORTS = ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_allgather_forward", "ra_rank_backward",
+           "ra_ulysses_relayout", "ra_plan",
            "ra_last_error", "ra_abi_version")
 
 
@@ -234,6 +238,40 @@ def ra_allgather_forward(q_local, k_global, v_global, o, lse, *, S: int, P: int,
                      1 if causal else 0, float(scale if scale is not None else D ** -0.5))
     _check(lib.ra_allgather_forward(ctypes.byref(d), _ptr(q_local), _ptr(k_global), _ptr(v_global),
                                     _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def ra_rank_backward(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_shards, delta, *,
+                     S: int, P: int, rank: int, order: str, causal: bool, scale: float | None = None,
+                     stream=None) -> None:
+    """Backward of rank ``rank``'s ring attention (bf16, D = 128).  q_local,
+    dout [B, S/P, Hq, D] bf16; k_shards, v_shards [P, B, S/P, Hkv, D] bf16; o,
+    lse from ra_rank_forward.  dq [B, S/P, Hq, D] float32 is written;
+    dk_shards, dv_shards [P, B, S/P, Hkv, D] float32 are added to; delta
+    [B, S/P, Hq] float32 is workspace (written with rowsum(dout * o))."""
+    torch = _torch()
+    _require(q_local, "q_local", ndim=4)
+    for t, n in ((k_shards, "k_shards"), (v_shards, "v_shards")):
+        _require(t, n, dtype=q_local.dtype, ndim=5)
+    _require(dout, "dout", dtype=q_local.dtype, ndim=4)
+    for t, n, nd in ((o, "o", 4), (lse, "lse", 3), (dq, "dq", 4), (dk_shards, "dk_shards", 5),
+                     (dv_shards, "dv_shards", 5), (delta, "delta", 3)):
+        _require(t, n, dtype=torch.float32, ndim=nd)
+    B, s_loc, Hq, D = q_local.shape
+    Hkv = k_shards.shape[3]
+    if P * s_loc != S:
+        raise ValueError("q_local must hold S/P rows")
+    shard = (P, B, s_loc, Hkv, D)
+    if any(tuple(t.shape) != shard for t in (k_shards, v_shards, dk_shards, dv_shards)):
+        raise ValueError("k_shards, v_shards, dk_shards, dv_shards must be [P, B, S/P, Hkv, D]")
+    if any(tuple(t.shape) != (B, s_loc, Hq, D) for t in (o, dout, dq)):
+        raise ValueError("o, dout and dq must be [B, S/P, Hq, D]")
+    if tuple(lse.shape) != (B, s_loc, Hq) or tuple(delta.shape) != (B, s_loc, Hq):
+        raise ValueError("lse and delta must be [B, S/P, Hq]")
+    d = ra_rank_desc(_dtype_code(q_local), B, Hq, Hkv, D, S, P, rank, ORDERS[order],
+                     1 if causal else 0, float(scale if scale is not None else D ** -0.5))
+    _check(lib.ra_rank_backward(ctypes.byref(d), _ptr(q_local), _ptr(k_shards), _ptr(v_shards), _ptr(o),
+                                _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk_shards), _ptr(dv_shards), _ptr(delta),
+                                _stream(stream)))
 
 
 def ra_lse_merge(o_a, lse_a, o_b, lse_b, o_out, lse_out, *, stream=None) -> None:

@@ -1,0 +1,652 @@
+// Backward of one ring step of blockwise attention on gfx950, bf16 inputs,
+// head dimension 128.
+//
+// What it computes: the gradient of sum(dO * O) for O = softmax(scale q K^T) V
+// over the visible keys of the step's key/value block, with the forward's
+// final log-sum-exp L of every query row: P = exp(scale q K^T - L) is then the
+// exact softmax weight of the whole sequence, so each step's share is exact
+// and the shares add up.  ringmaster's description asks for this backward on
+// the p2p ring, flash style, with the ring run in reverse ("Status", Ring row;
+// its note on the two Ring paths under "Why"); the formulas are the chain rule
+// through the softmax:
+//   dP = dO V^T,  dS = P * (dP - delta),  delta = rowsum(dO * O),
+//   dQ += scale dS K,  dK += scale dS^T Q,  dV += P^T dO,
+// with the G query heads of a group adding into their shared K/V head.
+//
+// Two kernels, so that no two workgroups add into the same rows:
+//   * dQ: a workgroup (4 waves) owns 128 query rows of one (batch, query
+//     head), 32 per wave, and walks the step's key tiles like the forward
+//     kernel: S^T = K Q^T and dP^T = V dO^T (K, V rows from LDS, Q^T and dO^T
+//     in registers), then dQ^T += K^T dS^T with K^T gathered by transposing
+//     LDS reads.
+//   * dK/dV: a workgroup owns 128 keys of one (batch, kv head), 32 per wave,
+//     with K^T in registers and V in LDS for the whole item, and walks the
+//     query tiles (32 rows) of every query head of the group that see them:
+//     S = Q K^T and dP = dO V^T (Q, dO rows from LDS), then dV^T += dO^T P and
+//     dK^T += Q^T dS with dO^T, Q^T by transposing LDS reads.  The softmax
+//     rows are spread over the accumulator registers here, so the rows' L and
+//     delta come from LDS as 16 values per lane.
+// Tiles are copied global -> LDS by buffer loads with the LDS bit.  One LDS
+// layout serves both read patterns: chunk c of row r sits at c ^ csw(r), with
+// csw(r) = 4 (r mod 4) + (r / 4) mod 4, which keeps the 16 rows of a row read
+// and the 4 rows x 4 chunks of a transposing read in distinct banks.
+#include "attn_common.h"
+
+namespace ra {
+namespace {
+
+using namespace dev;
+
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kD = 128;
+constexpr int kThreads = 256;
+constexpr int kRowB = 2 * kD;               // bytes of one bf16 row
+constexpr int kTileB = 32 * kRowB;          // a 32-row tile
+static_assert(kBK == 32, "32-row key tiles");
+
+__device__ inline unsigned csw(unsigned r) { return ((r & 3u) << 2) | ((r >> 2) & 3u); }
+
+// A-operand row read of unit u (16 columns): row_base ^ 32u, rows sigma(l%32).
+__device__ inline unsigned row_base_sigma(unsigned lane) {
+  const unsigned rho = sigma(lane & 31u);
+  return rho * kRowB + 16u * (csw(rho) ^ (lane >> 5));
+}
+// B-operand row read of unit u: row l%32 in natural order.
+__device__ inline unsigned row_base_plain(unsigned lane) {
+  const unsigned r = lane & 31u;
+  return r * kRowB + 16u * (csw(r) ^ (lane >> 5));
+}
+// Transposing reads: lane s of 16-lane group g reads row 8(g/2) + s/4 (b0)
+// and the row 4 below (b1) at column 32 db + 16 (g%2) + 4 (s%4); block db is
+// at b ^ 64 db and rows 16 further down at + 16 kRowB (csw repeats every 16).
+__device__ inline void tr_bases(unsigned lane, unsigned& b0, unsigned& b1) {
+  const unsigned g = lane >> 4, s = lane & 15u;
+  const unsigned r = 8u * (g >> 1) + (s >> 2);
+  const unsigned x = 2u * (g & 1u) + ((s & 3u) >> 1);
+  const unsigned e = 8u * (s & 1u);
+  b0 = r * kRowB + 16u * (x ^ csw(r)) + e;
+  b1 = (r + 4u) * kRowB + 16u * (x ^ csw(r + 4u)) + e;
+}
+__device__ inline bf16x8 tr_read(RA_LDS char* tile, unsigned b0, unsigned b1) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(tile + b0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(tile + b1));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// Tile offset (in the tensor) of the chunk a lane copies with DMA
+// instruction i of wave w (2 instructions of 1 KiB per wave fill 32 rows).
+__device__ inline unsigned dma_off(int w, int i, unsigned lane, unsigned row_bytes) {
+  const unsigned slot = (unsigned)(w * 2 + i) * 64u + lane;
+  const unsigned r = slot >> 4;
+  return r * row_bytes + 16u * ((slot & 15u) ^ csw(r));
+}
+
+__device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ inline float neg_inf_select(int d, float x) {
+  // x if d >= 0, else -inf (sign bit of d, no compare masks)
+  asm volatile("" : "+v"(d));
+  const unsigned m = (unsigned)(d >> 31);
+  return __uint_as_float((m & 0xff800000u) | (~m & __float_as_uint(x)));
+}
+
+// ===========================================================================
+// dQ kernel
+struct DqStage {
+  const char* khead;
+  const char* vhead;
+  unsigned row_bytes;
+  unsigned off[2];
+  int wave;
+
+  __device__ void init(const StepParams& p, const WorkItem& wi, int w, unsigned lane) {
+    row_bytes = (unsigned)(p.Hkv * kRowB);
+    const long long head = ((long long)wi.b * p.Sk * p.Hkv + wi.g) * (long long)kRowB;
+    khead = (const char*)p.k + head;
+    vhead = (const char*)p.v + head;
+    wave = w;
+    off[0] = dma_off(w, 0, lane, row_bytes);
+    off[1] = dma_off(w, 1, lane, row_bytes);
+  }
+  __device__ void issue(const TileCursor& c, RA_LDS char* kdst, RA_LDS char* vdst) const {
+    const long long o = c.local0 * (long long)row_bytes;
+    const int nrec = (c.count() - 1) * (int)row_bytes + kRowB;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(khead + o), (short)0, nrec, kRsrcWord3);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vhead + o), (short)0, nrec, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (RA_LDS void*)(kdst + (wave * 2 + i) * 1024), 16, (int)off[i], 0,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (RA_LDS void*)(vdst + (wave * 2 + i) * 1024), 16, (int)off[i], 0,
+                                               0, 0);
+    }
+  }
+};
+
+struct DqState {
+  bf16x8 q[kD / 16];    // Q^T operand: Q[row][16u + 8(l/32) .. +7]
+  bf16x8 d[kD / 16];    // dO^T operand, same layout
+  f32x16 acc[kD / 32];  // dQ^T accumulators
+  float lse2;           // L * log2(e) of the lane's row (+inf: the row has no weight)
+  float dlt;            // delta of the lane's row
+};
+
+template <int PAR>
+__device__ inline void dq_tile(DqState& st, const BwdParams& bp, const TilePlan& tp, const WorkItem& wi,
+                               const DqStage& stg, TileCursor& cur, int t, RA_LDS char* const* kbuf,
+                               RA_LDS char* const* vbuf, unsigned lane, int wave) {
+  const StepParams& p = bp.s;
+  const TileCursor ti = cur;
+  if (t + 1 < tp.n) {
+    cur.advance(tp);
+    stg.issue(cur, kbuf[PAR ^ 1], vbuf[PAR ^ 1]);
+  }
+  const unsigned rb = row_base_sigma(lane);
+  f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+  for (int u = 0; u < kD / 16; ++u) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(kbuf[PAR], rb ^ (32u * u)));
+    const bf16x8 b = __builtin_bit_cast(bf16x8, lds_load16(vbuf[PAR], rb ^ (32u * u)));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.q[u], s, 0, 0, 0);
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, st.d[u], dp, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int L = (int)(lane >> 5);
+  if (ti.masked()) {
+    // key 16(r/8) + 8L + r%8 of the tile is visible to the lane's row iff it
+    // is below lim
+    const long long d0 = wi.qglob0 - ti.glob0 + 1;
+    const int dc = p.causal ? (int)max(-1024LL, min(1024LL, d0)) : 1024;
+    const int lim = min(ti.count(), max(0, dc + 32 * wave + (int)(lane & 31u)));
+    const int lim_l = lim - 8 * L - 1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = neg_inf_select(lim_l - (16 * (r >> 3) + (r & 7)), s[r]);
+  }
+  // P^T = exp2(S^T sl2 - L log2 e); dS^T = P^T (dP^T - delta), rounded to bf16
+  bf16x8 dsb[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    f32x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hf + e], p.sl2, -st.lse2));
+      x[e] = pr * (dp[8 * hf + e] - st.dlt);
+    }
+    dsb[hf] = __builtin_convertvector(x, bf16x8);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // dQ^T += K^T dS^T
+  unsigned b0, b1;
+  tr_bases(lane, b0, b1);
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) {
+      const bf16x8 a = tr_read(kbuf[PAR], (b0 ^ (64u * db)) + 16u * kRowB * hf, (b1 ^ (64u * db)) + 16u * kRowB * hf);
+      st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[hf], st.acc[db], 0, 0, 0);
+    }
+  wait_loads();
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(BwdParams bp) {
+  const StepParams& p = bp.s;
+  __shared__ __attribute__((aligned(16))) char k0_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char k1_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char v0_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char v1_raw[kTileB];
+  RA_LDS char* const kbuf[2] = {(RA_LDS char*)k0_raw, (RA_LDS char*)k1_raw};
+  RA_LDS char* const vbuf[2] = {(RA_LDS char*)v0_raw, (RA_LDS char*)v1_raw};
+  const unsigned lane = threadIdx.x & 63u;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  WorkItem wi;
+  if (!decode_work<kBwdRows>(p, wi)) return;
+  const int row = 32 * wave + (int)(lane & 31u);
+  const bool row_ok = row < wi.qrows;
+  const long long orow = ((long long)wi.b * p.Sq + wi.qlocal0 + row) * p.Hq + wi.h;  // (b, row, h)
+  const int dsub = 4 * (int)(lane >> 5);
+  const TilePlan tp = plan_tiles(p, wi.qglob0, wi.qglob0 + wi.qrows - 1);
+  if (tp.n == 0) {
+    if (!p.accum && row_ok) {
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *(float4*)(bp.dq + orow * kD + 32 * db + 8 * j + dsub) = float4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+
+  DqStage stg;
+  stg.init(p, wi, wave, lane);
+  TileCursor cur;
+  cur.first(tp);
+  stg.issue(cur, kbuf[0], vbuf[0]);
+
+  DqState st;
+  {
+    const uint16_t* qrow = (const uint16_t*)p.q + orow * kD;
+    const uint16_t* drow = (const uint16_t*)bp.dout + orow * kD;
+#pragma unroll
+    for (int u = 0; u < kD / 16; ++u) {
+      st.q[u] = row_ok ? *(const bf16x8*)(qrow + 16 * u + 8 * (lane >> 5)) : bf16x8{};
+      st.d[u] = row_ok ? *(const bf16x8*)(drow + 16 * u + 8 * (lane >> 5)) : bf16x8{};
+    }
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) st.acc[db] = f32x16{};
+    const float l = row_ok ? bp.lse[orow] : kNegInf;
+    st.lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+    st.dlt = row_ok ? bp.delta[orow] : 0.f;
+  }
+  wait_loads();
+  __syncthreads();
+
+  int t = 0;
+  for (; t + 1 < tp.n; t += 2) {
+    dq_tile<0>(st, bp, tp, wi, stg, cur, t, kbuf, vbuf, lane, wave);
+    dq_tile<1>(st, bp, tp, wi, stg, cur, t + 1, kbuf, vbuf, lane, wave);
+  }
+  if (t < tp.n) dq_tile<0>(st, bp, tp, wi, stg, cur, t, kbuf, vbuf, lane, wave);
+
+  if (!row_ok) return;
+  float* dst = bp.dq + orow * kD;
+#pragma unroll
+  for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x16& a = st.acc[db];
+      float4 v = {a[4 * j] * p.scale, a[4 * j + 1] * p.scale, a[4 * j + 2] * p.scale, a[4 * j + 3] * p.scale};
+      float* ptr = dst + 32 * db + 8 * j + dsub;
+      if (p.accum) {
+        const float4 r = *(const float4*)ptr;
+        v.x += r.x;
+        v.y += r.y;
+        v.z += r.z;
+        v.w += r.w;
+      }
+      *(float4*)ptr = v;
+    }
+}
+
+// ===========================================================================
+// dK/dV kernel
+
+// Query tiles (32 rows) of every head of the group that see a key tile: per
+// query span, the tiles from the first row at or after the tile's first key
+// (causal) to the span's end.
+struct QPlan {
+  int tbeg[2], tend[2];  // tile range per span
+  int per_head;          // tiles per query head
+  int n;                 // G * per_head
+};
+
+struct QCursor {
+  int hh;       // query head within the group
+  int span;     // 0 or 1
+  int tile;     // tile index within the span
+  __device__ void first(const QPlan& qp) {
+    hh = 0;
+    span = qp.tend[0] > qp.tbeg[0] ? 0 : 1;
+    tile = span ? qp.tbeg[1] : qp.tbeg[0];
+  }
+  __device__ void advance(const QPlan& qp) {
+    ++tile;
+    const int end = span ? qp.tend[1] : qp.tend[0];
+    if (tile < end) return;
+    if (span == 0 && qp.tend[1] > qp.tbeg[1]) {
+      span = 1;
+      tile = qp.tbeg[1];
+      return;
+    }
+    ++hh;
+    span = qp.tend[0] > qp.tbeg[0] ? 0 : 1;
+    tile = span ? qp.tbeg[1] : qp.tbeg[0];
+  }
+};
+
+struct KvItem {
+  int b, g;
+  int kcount;            // keys of the item that exist (<= kBwdKeys)
+  long long klocal0;     // first local key row
+  long long kglob0;      // its global position
+};
+
+__device__ inline bool decode_kv(const BwdParams& bp, KvItem& it) {
+  const StepParams& p = bp.s;
+  const int w = (blockIdx.x & 7) * bp.per_xcd_kv + (blockIdx.x >> 3);
+  if (w >= bp.n_kwork) return false;
+  const int kt = w % bp.n_ktiles;  // earlier keys first: causal rows see them most
+  const int rest = w / bp.n_ktiles;
+  it.g = rest % p.Hkv;
+  it.b = rest / p.Hkv;
+  const int ks = kt < bp.kt_span0 ? 0 : 1;
+  const long long k_in = (long long)(ks ? kt - bp.kt_span0 : kt) * kBwdKeys;
+  it.kcount = (int)min((long long)kBwdKeys, p.ks_len[ks] - k_in);
+  it.klocal0 = p.ks_off[ks] + k_in;
+  it.kglob0 = p.ks_start[ks] + k_in;
+  return true;
+}
+
+__device__ inline QPlan plan_q(const StepParams& p, long long kglob0) {
+  QPlan qp;
+  qp.per_head = 0;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    int b = 0, e = 0;
+    if (s < p.nqs) {
+      long long first = 0;
+      if (p.causal) first = max(0LL, kglob0 - p.qs_start[s]);
+      const long long len = p.qs_len[s];
+      if (first < len) {
+        b = (int)(first / 32);
+        e = (int)((len + 31) / 32);
+      }
+    }
+    qp.tbeg[s] = b;
+    qp.tend[s] = e;
+    qp.per_head += e - b;
+  }
+  qp.n = p.G * qp.per_head;
+  return qp;
+}
+
+struct KvStage {
+  const char* qbase;     // row 0 of (batch b, query head 0) in Q
+  const char* dbase;     // same in dO
+  const float* lbase;    // (b, row 0, head 0) in L
+  const float* tbase;    // same in delta
+  unsigned row_bytes;    // Hq * 2D
+  unsigned off[2];
+  int wave, Hq;
+
+  __device__ void init(const BwdParams& bp, const KvItem& it, int w, unsigned lane) {
+    const StepParams& p = bp.s;
+    Hq = p.Hq;
+    row_bytes = (unsigned)(p.Hq * kRowB);
+    const long long base = (long long)it.b * p.Sq * p.Hq;
+    qbase = (const char*)p.q + base * kRowB;
+    dbase = (const char*)bp.dout + base * kRowB;
+    lbase = bp.lse + base;
+    tbase = bp.delta + base;
+    wave = w;
+    off[0] = dma_off(w, 0, lane, row_bytes);
+    off[1] = dma_off(w, 1, lane, row_bytes);
+  }
+  // Query tile `c` of head h: 32 rows of Q and dO, and L, delta of the rows
+  // (lanes 0..63 of one 4-byte copy each; rows past the tile's end read 0).
+  __device__ void issue(const StepParams& p, const QPlan& qp, const QCursor& c, int g, unsigned lane,
+                        RA_LDS char* qdst, RA_LDS char* ddst, RA_LDS char* ldst) const {
+    (void)qp;
+    const int h = g * p.G + c.hh;
+    const long long qin = (long long)c.tile * 32;
+    const long long local0 = (c.span ? p.qs_off[1] : p.qs_off[0]) + qin;
+    const int count = (int)min(32LL, (c.span ? p.qs_len[1] : p.qs_len[0]) - qin);
+    const long long o = local0 * (long long)row_bytes + (long long)h * kRowB;
+    const int nrec = (count - 1) * (int)row_bytes + kRowB;
+    const auto rq = __builtin_amdgcn_make_buffer_rsrc((void*)(qbase + o), (short)0, nrec, kRsrcWord3);
+    const auto rd = __builtin_amdgcn_make_buffer_rsrc((void*)(dbase + o), (short)0, nrec, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (RA_LDS void*)(qdst + (wave * 2 + i) * 1024), 16, (int)off[i], 0,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (RA_LDS void*)(ddst + (wave * 2 + i) * 1024), 16, (int)off[i], 0,
+                                               0, 0);
+    }
+    if (wave < 2) {
+      // wave 0: L of rows 0..63 into ldst[0, 256); wave 1: delta into [256, 512)
+      const float* src = (wave == 0 ? lbase : tbase) + local0 * Hq + h;
+      const int nr = ((count - 1) * Hq + 1) * 4;
+      const auto rl = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nr, kRsrcWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (RA_LDS void*)(ldst + wave * 256), 4, (int)(lane * (unsigned)Hq * 4u),
+                                               0, 0, 0);
+    }
+  }
+};
+
+struct KvState {
+  bf16x8 k[kD / 16];     // K^T operand: K[key l%32][16u + 8(l/32) .. +7]
+  f32x16 dk[kD / 32];    // dK^T accumulators
+  f32x16 dv[kD / 32];    // dV^T accumulators
+};
+
+template <int PAR>
+__device__ inline void kv_tile(KvState& st, const BwdParams& bp, const QPlan& qp, const KvItem& it,
+                               const KvStage& stg, QCursor& cur, int t, RA_LDS char* const* qbuf,
+                               RA_LDS char* const* dbuf, RA_LDS char* const* lbuf, RA_LDS char* vt,
+                               unsigned lane, int wave) {
+  const StepParams& p = bp.s;
+  const QCursor ci = cur;
+  if (t + 1 < qp.n) {
+    cur.advance(qp);
+    stg.issue(p, qp, cur, it.g, lane, qbuf[PAR ^ 1], dbuf[PAR ^ 1], lbuf[PAR ^ 1]);
+  }
+  // this wave's keys against the tile's rows
+  const long long qin = (long long)ci.tile * 32;
+  const long long qglob = (ci.span ? p.qs_start[1] : p.qs_start[0]) + qin;
+  const int qcount = (int)min(32LL, (ci.span ? p.qs_len[1] : p.qs_len[0]) - qin);
+  const long long kwg = it.kglob0 + 32 * wave;
+  const bool has_keys = 32 * wave < it.kcount;
+  const bool live = has_keys && (!p.causal || kwg <= qglob + qcount - 1);
+  if (live) {
+    const unsigned rb = row_base_sigma(lane);
+    const unsigned vb = row_base_plain(lane) + (unsigned)(32 * wave * kRowB);
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int u = 0; u < kD / 16; ++u) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(qbuf[PAR], rb ^ (32u * u)));
+      const bf16x8 b = __builtin_bit_cast(bf16x8, lds_load16(dbuf[PAR], rb ^ (32u * u)));
+      const bf16x8 vv = __builtin_bit_cast(bf16x8, lds_load16(vt, vb ^ (32u * u)));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.k[u], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, vv, dp, 0, 0, 0);
+    }
+    // operand reads one unit ahead of their MFMAs (bounds the registers in flight)
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+    for (int u = 1; u < kD / 16; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // rows of register r: 16(r/8) + 8L + r%8 of the tile
+    const int L = (int)(lane >> 5);
+    const int key = (int)(lane & 31u);
+    if (p.causal && kwg + 31 > qglob) {
+      // row i sees key j iff qglob + i >= kwg + j
+      const int dd = (int)max(-1024LL, min(1024LL, qglob - kwg)) + 8 * L - key;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = neg_inf_select(dd + 16 * (r >> 3) + (r & 7), s[r]);
+    }
+    const RA_LDS float* lt = (const RA_LDS float*)lbuf[PAR];
+    unsigned b0, b1;
+    tr_bases(lane, b0, b1);
+    // one 16-row half at a time: P and dS of rows 16hf .. 16hf+15, then
+    // dV^T += dO^T P and dK^T += Q^T dS over those rows
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 l0 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L);
+      const f32x4 l1 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L + 4);
+      const f32x4 t0 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L);
+      const f32x4 t1 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L + 4);
+      const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+      const float tv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+      f32x8 x, y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // rows past the tile's end and rows with no weight (L = -inf) give 0
+        const bool ok = 16 * hf + 8 * L + e < qcount && lv[e] != kNegInf;
+        const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e)) : 0.f;
+        x[e] = pr;
+        y[e] = pr * (dp[8 * hf + e] - tv[e]);
+      }
+      const bf16x8 pb = __builtin_convertvector(x, bf16x8);
+      const bf16x8 dsb = __builtin_convertvector(y, bf16x8);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db) {
+        const unsigned o0 = (b0 ^ (64u * db)) + 16u * kRowB * hf, o1 = (b1 ^ (64u * db)) + 16u * kRowB * hf;
+        const bf16x8 ad = tr_read(dbuf[PAR], o0, o1);
+        const bf16x8 aq = tr_read(qbuf[PAR], o0, o1);
+        st.dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, pb, st.dv[db], 0, 0, 0);
+        st.dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsb, st.dk[db], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_loads();
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dkdv_kernel(BwdParams bp) {
+  const StepParams& p = bp.s;
+  __shared__ __attribute__((aligned(16))) char q0_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char q1_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char d0_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char d1_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char l0_raw[512];
+  __shared__ __attribute__((aligned(16))) char l1_raw[512];
+  __shared__ __attribute__((aligned(16))) char v_raw[kBwdKeys * kRowB];
+  RA_LDS char* const qbuf[2] = {(RA_LDS char*)q0_raw, (RA_LDS char*)q1_raw};
+  RA_LDS char* const dbuf[2] = {(RA_LDS char*)d0_raw, (RA_LDS char*)d1_raw};
+  RA_LDS char* const lbuf[2] = {(RA_LDS char*)l0_raw, (RA_LDS char*)l1_raw};
+  RA_LDS char* const vt = (RA_LDS char*)v_raw;
+  const unsigned lane = threadIdx.x & 63u;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  KvItem it;
+  if (!decode_kv(bp, it)) return;
+  const QPlan qp = plan_q(p, it.kglob0);
+  if (qp.n == 0) return;
+
+  // V of the item's keys into LDS (32 rows per wave, the tile layout), K^T
+  // operands into registers.
+  const unsigned krow_bytes = (unsigned)(p.Hkv * kRowB);
+  const long long khead = ((long long)it.b * p.Sk * p.Hkv + it.g) * (long long)kRowB;
+  const int my_keys = min(32, it.kcount - 32 * wave);
+  if (my_keys > 0) {
+    const char* vsrc = (const char*)p.v + khead + (it.klocal0 + 32 * wave) * (long long)krow_bytes;
+    const int nrec = (my_keys - 1) * (int)krow_bytes + kRowB;
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)vsrc, (short)0, nrec, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // slot i*64 + lane of the wave's 32-row block
+      const unsigned slot = (unsigned)i * 64u + lane;
+      const unsigned r = slot >> 4;
+      const unsigned o = r * krow_bytes + 16u * ((slot & 15u) ^ csw(r));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (RA_LDS void*)(vt + 32 * wave * kRowB + i * 1024), 16, (int)o, 0, 0,
+                                               0);
+    }
+  }
+  KvState st;
+  {
+    const int key = 32 * wave + (int)(lane & 31u);
+    const bool kok = key < it.kcount;
+    const uint16_t* krow = (const uint16_t*)((const char*)p.k + khead + (it.klocal0 + key) * (long long)krow_bytes);
+#pragma unroll
+    for (int u = 0; u < kD / 16; ++u) st.k[u] = kok ? *(const bf16x8*)(krow + 16 * u + 8 * (lane >> 5)) : bf16x8{};
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) st.dk[db] = st.dv[db] = f32x16{};
+  }
+
+  KvStage stg;
+  stg.init(bp, it, wave, lane);
+  QCursor cur;
+  cur.first(qp);
+  stg.issue(p, qp, cur, it.g, lane, qbuf[0], dbuf[0], lbuf[0]);
+  wait_loads();
+  __syncthreads();
+
+  int t = 0;
+  for (; t + 1 < qp.n; t += 2) {
+    kv_tile<0>(st, bp, qp, it, stg, cur, t, qbuf, dbuf, lbuf, vt, lane, wave);
+    kv_tile<1>(st, bp, qp, it, stg, cur, t + 1, qbuf, dbuf, lbuf, vt, lane, wave);
+  }
+  if (t < qp.n) kv_tile<0>(st, bp, qp, it, stg, cur, t, qbuf, dbuf, lbuf, vt, lane, wave);
+
+  // dK = scale dS^T Q and dV = P^T dO of the wave's keys, added to the tensors
+  const int key = 32 * wave + (int)(lane & 31u);
+  if (key >= it.kcount) return;
+  const long long krow = ((long long)it.b * p.Sk + it.klocal0 + key) * p.Hkv + it.g;
+  float* dkp = bp.dk + krow * kD;
+  float* dvp = bp.dv + krow * kD;
+  const int dsub = 4 * (int)(lane >> 5);
+#pragma unroll
+  for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 32 * db + 8 * j + dsub;
+      const f32x16& a = st.dk[db];
+      const f32x16& b = st.dv[db];
+      float4 rk = *(const float4*)(dkp + c);
+      float4 rv = *(const float4*)(dvp + c);
+      rk.x += a[4 * j] * p.scale;
+      rk.y += a[4 * j + 1] * p.scale;
+      rk.z += a[4 * j + 2] * p.scale;
+      rk.w += a[4 * j + 3] * p.scale;
+      rv.x += b[4 * j];
+      rv.y += b[4 * j + 1];
+      rv.z += b[4 * j + 2];
+      rv.w += b[4 * j + 3];
+      *(float4*)(dkp + c) = rk;
+      *(float4*)(dvp + c) = rv;
+    }
+}
+
+// ===========================================================================
+// delta = rowsum(dO * O): 16 lanes per row of 128, 8 elements per lane.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(long long rows, const T* __restrict__ dout,
+                                                        const float* __restrict__ o, float* __restrict__ delta) {
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const float* orow = o + row * kD + 8 * part;
+    const float4 o0 = *(const float4*)orow;
+    const float4 o1 = *(const float4*)(orow + 4);
+    float dv[8];
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 d = *(const bf16x8*)((const uint16_t*)dout + row * kD + 8 * part);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dv[e] = (float)d[e];
+    } else {
+      const float4 d0 = *(const float4*)((const float*)dout + row * kD + 8 * part);
+      const float4 d1 = *(const float4*)((const float*)dout + row * kD + 8 * part + 4);
+      dv[0] = d0.x, dv[1] = d0.y, dv[2] = d0.z, dv[3] = d0.w;
+      dv[4] = d1.x, dv[5] = d1.y, dv[6] = d1.z, dv[7] = d1.w;
+    }
+    acc = dv[0] * o0.x + dv[1] * o0.y + dv[2] * o0.z + dv[3] * o0.w + dv[4] * o1.x + dv[5] * o1.y + dv[6] * o1.z +
+          dv[7] * o1.w;
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (row < rows && part == 0) delta[row] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s) {
+  if (p.s.n_work > 0) hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(8 * p.s.per_xcd), dim3(kThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.n_kwork > 0) hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(8 * p.per_xcd_kv), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_delta(long long rows, int D, int dtype, const void* dout, const float* o, float* delta,
+                            hipStream_t s) {
+  if (D != kD) return hipErrorInvalidValue;
+  if (rows <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((rows + 15) / 16);
+  if (dtype == 1)
+    hipLaunchKernelGGL(bwd_delta_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, rows, (const uint16_t*)dout, o,
+                       delta);
+  else
+    hipLaunchKernelGGL(bwd_delta_kernel<float>, dim3(blocks), dim3(256), 0, s, rows, (const float*)dout, o, delta);
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -78,8 +78,6 @@ struct Layout {
   __device__ static unsigned vsw(unsigned r) { return (4u * ((r & 3u) >> (kCPR == 16 ? 0 : 1))) & (kCPR - 1); }
 };
 
-__device__ inline unsigned sigma(unsigned i) { return (i & ~12u) | ((i & 4u) << 1) | ((i & 8u) >> 1); }
-
 template <int D>
 struct WaveState {
   bf16x8 q[kQB][D / 16];      // Q^T operands: Q[row][16u + 8(l/32) .. +7]
@@ -128,55 +126,6 @@ struct Lane {
     return r * row_bytes + 16u * ((slot % Ly::kCPR) ^ (v ? Ly::vsw(r) : Ly::ksw(r)));
   }
 };
-
-// Walks the key tiles of a work item in the order the tile plan fixes (the
-// unmasked tiles of each span, then the masked ones), one scalar update per
-// tile; only the first tile of a segment recomputes from the plan.
-struct TileCursor {
-  long long local0, glob0;  // first local row of the tile, its global position
-  long long vis;            // rows of the span visible from local0 on
-  int rem;                  // tiles left in the segment, this one included
-  int seg;                  // 0, 1: unmasked tiles of span 0, 1; 2, 3: masked
-
-  __device__ int count() const { return (int)min((long long)kBK, vis); }
-  __device__ bool masked() const { return seg >= 2; }
-
-  __device__ bool enter(const TilePlan& tp, int j) {
-    // selects only: a run-time index into the plan's arrays would put the
-    // plan in scratch memory
-    const bool s = j & 1;
-    const int nf = s ? tp.nf[1] : tp.nf[0];
-    const int n = j < 2 ? nf : (s ? tp.nr[1] : tp.nr[0]);
-    if (n == 0) return false;
-    const long long kin = j < 2 ? 0 : (long long)nf * kBK;
-    local0 = (s ? tp.off[1] : tp.off[0]) + kin;
-    glob0 = (s ? tp.start[1] : tp.start[0]) + kin;
-    vis = (s ? tp.hi[1] : tp.hi[0]) - kin;
-    rem = n;
-    seg = j;
-    return true;
-  }
-  __device__ void first(const TilePlan& tp) {
-    for (int j = 0; j < 4; ++j)
-      if (enter(tp, j)) return;
-  }
-  __device__ void advance(const TilePlan& tp) {
-    if (rem > 1) {
-      --rem;
-      local0 += kBK;
-      glob0 += kBK;
-      vis -= kBK;
-      return;
-    }
-    for (int j = seg + 1; j < 4; ++j)
-      if (enter(tp, j)) return;
-  }
-};
-
-// Buffer resource over the key rows of a tile of K or V for one head: the
-// record ends with the last row the tile may see, so loads of rows past
-// `count` (a span's ragged end) return 0 and never leave the tensor.
-constexpr int kRsrcWord3 = 0x00020000;
 
 // DMA staging of K and V tiles for one work item.
 template <int D>

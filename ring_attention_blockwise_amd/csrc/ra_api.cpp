@@ -334,6 +334,72 @@ int ra_allgather_forward(const ra_rank_desc* d, const void* q_local, const void*
   return ok();
 }
 
+int ra_rank_backward(const ra_rank_desc* d, const void* q_local, const void* k_shards, const void* v_shards,
+                     const float* o, const float* lse, const void* dout, float* dq, float* dk_shards,
+                     float* dv_shards, float* delta, void* stream) {
+  if (!d) return fail(RA_E_INVAL, "descriptor is NULL");
+  int rc = check_ring(d->order, d->S, d->P, d->rank);
+  if (rc) return rc;
+  if (d->dtype != RA_DTYPE_BF16 || d->D != 128)
+    return fail(RA_E_UNSUPPORTED, "the backward pass is built for bf16 with D = 128");
+  const int64_t s_loc = d->S / d->P;
+  ra_step_desc sd;
+  sd.dtype = d->dtype;
+  sd.B = d->B;
+  sd.Hq = d->Hq;
+  sd.Hkv = d->Hkv;
+  sd.D = d->D;
+  sd.Sq = s_loc;
+  sd.Sk = s_loc;
+  sd.causal = d->causal;
+  sd.scale = d->scale;
+  const Spans qs = rank_spans(d->order, d->S, d->P, d->rank);
+  sd.n_qspans = qs.n;
+  for (int i = 0; i < 2; ++i) sd.qspans[i] = i < qs.n ? qs.s[i] : ra_span{0, 0};
+  sd.n_kspans = qs.n;
+  for (int i = 0; i < 2; ++i) sd.kspans[i] = sd.qspans[i];
+  rc = check_step(&sd, q_local, k_shards, v_shards, dq, lse, RA_STEP_INIT);
+  if (rc) return rc;
+  if (s_loc == 0) return ok();
+  if (!o || !dout || !dk_shards || !dv_shards || !delta) return fail(RA_E_INVAL, "NULL pointer");
+  if (!aligned(o, 16) || !aligned(dout, 16) || !aligned(dk_shards, 16) || !aligned(dv_shards, 16) ||
+      !aligned(delta, 4))
+    return fail(RA_E_INVAL, "o, dout, dk_shards and dv_shards must be 16-byte aligned, delta 4-byte aligned");
+  const int64_t rows = (int64_t)d->B * s_loc * d->Hq;
+  hipError_t e = ra::launch_bwd_delta(rows, d->D, 1, dout, o, delta, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RA_E_HIP, "delta launch failed: %s", hipGetErrorString(e));
+  const int64_t shard_elems = (int64_t)d->B * s_loc * d->Hkv * d->D;
+  for (int32_t s = 0; s < d->P; ++s) {
+    const int32_t src = ring_src(d->rank, s, d->P);
+    const Spans ks = rank_spans(d->order, d->S, d->P, src);
+    sd.n_kspans = ks.n;
+    for (int i = 0; i < 2; ++i) sd.kspans[i] = i < ks.n ? ks.s[i] : ra_span{0, 0};
+    const char* kp = (const char*)k_shards + (size_t)src * shard_elems * 2;
+    const char* vp = (const char*)v_shards + (size_t)src * shard_elems * 2;
+    ra::BwdParams bp;
+    if (!build_params(&sd, q_local, kp, vp, nullptr, nullptr, s > 0, &bp.s)) continue;
+    // the dQ kernel's query tiles are kBwdRows rows
+    bp.s.qt_span0 = (int)((bp.s.qs_len[0] + ra::kBwdRows - 1) / ra::kBwdRows);
+    bp.s.n_qtiles = bp.s.qt_span0 + (int)((bp.s.qs_len[1] + ra::kBwdRows - 1) / ra::kBwdRows);
+    bp.s.n_work = bp.s.B * bp.s.Hq * bp.s.n_qtiles;
+    bp.s.per_xcd = (bp.s.n_work + 7) / 8;
+    bp.dout = dout;
+    bp.lse = lse;
+    bp.delta = delta;
+    bp.dq = dq;
+    bp.dk = dk_shards + (size_t)src * shard_elems;
+    bp.dv = dv_shards + (size_t)src * shard_elems;
+    // key tiles of kBwdKeys keys over the block's key spans, for the dK/dV kernel
+    bp.kt_span0 = (int)((bp.s.ks_len[0] + ra::kBwdKeys - 1) / ra::kBwdKeys);
+    bp.n_ktiles = bp.kt_span0 + (int)((bp.s.ks_len[1] + ra::kBwdKeys - 1) / ra::kBwdKeys);
+    bp.n_kwork = bp.s.B * bp.s.Hkv * bp.n_ktiles;
+    bp.per_xcd_kv = (bp.n_kwork + 7) / 8;
+    e = ra::launch_attn_bwd_bf16(bp, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(RA_E_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
 int ra_lse_merge(int64_t rows, int32_t D, const float* o_a, const float* lse_a, const float* o_b,
                  const float* lse_b, float* o_out, float* lse_out, void* stream) {
   if (rows < 0) return fail(RA_E_INVAL, "rows must be >= 0");

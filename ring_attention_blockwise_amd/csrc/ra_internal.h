@@ -46,6 +46,34 @@ hipError_t launch_attn_step(const StepParams& p, int dtype, int D, hipStream_t s
 hipError_t launch_attn_step_f32(const StepParams& p, int D, hipStream_t s);
 hipError_t launch_attn_step_bf16(const StepParams& p, int D, hipStream_t s);
 
+// Backward of one ring step for bf16 inputs, D = 128: the dQ kernel (query
+// tiles of kBwdRows rows, loops over the step's key tiles) and the dK/dV
+// kernel (key tiles of kBwdKeys keys, loops over the query heads of their
+// group and the visible query tiles).
+constexpr int kBwdRows = 128;
+constexpr int kBwdKeys = 128;
+
+struct BwdParams {
+  StepParams s;          // q, k, v, spans, shapes, causal, scale; s.accum: dQ INIT / ACCUM;
+                         // s.n_qtiles, qt_span0, n_work, per_xcd: the dQ kernel's query tiles
+  const void* dout;      // dO, the layout and dtype of q
+  const float* lse;      // forward LSE (natural log), [B, Sq, Hq]
+  const float* delta;    // rowsum(dO * O), [B, Sq, Hq]
+  float* dq;             // [B, Sq, Hq, D]: written (INIT) or added to (ACCUM)
+  float* dk;             // [B, Sk, Hkv, D]: added to
+  float* dv;             // [B, Sk, Hkv, D]: added to
+  int kt_span0;          // key tiles in listed key span 0
+  int n_ktiles;          // key tiles per (batch, kv head)
+  int n_kwork;           // B * Hkv * n_ktiles
+  int per_xcd_kv;        // ceil(n_kwork / 8)
+};
+
+hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s);
+// delta[row] = sum_d dO[row, d] * O[row, d] over rows of D elements; dO bf16
+// (dtype 1) or f32 (dtype 0), O f32.
+hipError_t launch_bwd_delta(long long rows, int D, int dtype, const void* dout, const float* o, float* delta,
+                            hipStream_t s);
+
 hipError_t launch_lse_merge(long long rows, int D, const float* o_a,
                             const float* lse_a, const float* o_b,
                             const float* lse_b, float* o_out, float* lse_out,

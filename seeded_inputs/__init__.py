@@ -30,7 +30,7 @@ from .workloads import WORKLOADS, Workload, workload  # noqa: F401
 
 BASE_SEED = 20261203
 TOKENS_PER_BLOCK = 128
-TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_DO = 0, 1, 2, 3
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
