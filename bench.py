@@ -175,6 +175,43 @@ def time_allgather(ra, w, rank, ring_ms, reps=5):
             "ring_over_allgather": ring_ms / ms}
 
 
+def time_backward(ra, w, rank, reps=3):
+    """The backward pass of the same rank (reverse ring, dQ and dK/dV
+    kernels per step), after one forward.  Algorithmic work: 2.5 times the
+    forward's (five products per visible pair instead of two)."""
+    import torch
+    import seeded_inputs as si
+    q, ks, vs, o, lse = build_inputs(ra, w, rank)
+    do = to_device(si.tokens(w.seed_id, si.TENSOR_DO, w.B, w.S, w.Hq, w.D,
+                             ra.rank_spans(w.order, w.S, w.P, rank), w.dtype), w.dtype)
+    s_loc = w.S // w.P
+    dq = torch.empty((w.B, s_loc, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((w.P, w.B, s_loc, w.Hkv, w.D), dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    delta = torch.empty((w.B, s_loc, w.Hq), dtype=torch.float32, device="cuda")
+    kw = dict(S=w.S, P=w.P, rank=rank, order=w.order, causal=w.causal, scale=w.scale)
+    ra.ra_rank_forward(q, ks, vs, o, lse, **kw)
+
+    def run():
+        ra.ra_rank_backward(q, ks, vs, o, lse, do, dq, dk, dv, delta, **kw)
+
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = 2.5 * algorithmic_flops(w, rank)
+    ok = bool(torch.isfinite(dq).all().item() and torch.isfinite(dk).all().item())
+    del q, ks, vs, o, lse, do, dq, dk, dv, delta
+    torch.cuda.empty_cache()
+    return {"kernel": "rank_backward", "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "frac_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "finite": ok}
+
+
 def time_merge(ra, rows, D, reps=20):
     """Standalone merge, rotating buffer sets so the working set exceeds the
     256 MB Infinity Cache."""
@@ -307,6 +344,8 @@ def main():
     aux = []
     if not args.no_aux:
         aux.append(time_allgather(ra, w, rank, ms))
+        if w.dtype == "bf16" and w.D == 128:
+            aux.append(time_backward(ra, w, rank))
         aux.append(time_merge(ra, w.B * (w.S // w.P) * w.Hq, w.D))
         aux.append(time_relayout(ra, 2, 8192, 16, 128, 8))
         for a in aux:
