@@ -264,6 +264,41 @@ def time_relayout(ra, B, s_loc, H, D, P_u, reps=20):
             "frac_hbm": moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
+def time_ulysses_pieces(ra, B, s_loc, H, D, P_u, reps=20):
+    """Fused Q/K/V messages of the Ulysses all-to-all (one launch for three
+    bf16 tensors): the sender's pack of [B, s_loc, H, D] shards into head
+    blocks, and the receiver's regrouping of the pieces into all
+    P_u * s_loc tokens of its H / P_u heads.  Buffer sets rotate past the
+    Infinity Cache."""
+    import torch
+    nbytes = B * s_loc * H * D * 2
+    nsets = max(2, int(np.ceil(1.2e9 / (6 * nbytes))))
+    res = []
+    for group, name, shape, to_pieces in (
+            (ra.RA_GROUP_HEADS, "ulysses_pack_qkv", (B, s_loc, H, D), True),
+            (ra.RA_GROUP_SEQ, "ulysses_regroup_qkv", (B, P_u * s_loc, H // P_u, D), False)):
+        sets = [([torch.randn(shape, device="cuda").to(torch.bfloat16) for _ in range(3)],
+                 torch.empty(3 * nbytes, dtype=torch.uint8, device="cuda")) for _ in range(nsets)]
+        for xs, buf in sets:
+            ra.ra_ulysses_pieces(xs, buf, P_u, to_pieces=to_pieces, group=group)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            xs, buf = sets[i % nsets]
+            ra.ra_ulysses_pieces(xs, buf, P_u, to_pieces=to_pieces, group=group)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        moved = 2 * 3 * nbytes
+        res.append({"kernel": name, "shape": list(shape), "tensors": 3, "P_u": P_u, "bytes": moved,
+                    "us": ms * 1e3, "GB/s": moved / (ms * 1e-3) / 1e9,
+                    "frac_hbm": moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS})
+        del sets
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, rank, target_s=15.0):
     """The CPU oracle, as it stands, on a bounded sample of rank ``rank``'s rows
     (all heads), scaled to TFLOP/s by the algorithmic FLOPs of those rows."""
@@ -348,6 +383,7 @@ def main():
             aux.append(time_backward(ra, w, rank))
         aux.append(time_merge(ra, w.B * (w.S // w.P) * w.Hq, w.D))
         aux.append(time_relayout(ra, 2, 8192, 16, 128, 8))
+        aux.extend(time_ulysses_pieces(ra, 2, 8192, 16, 128, 8))
         for a in aux:
             if "GB/s" in a:
                 print(f"[bench] {a['kernel']}: {a['us']:.1f} us, {a['GB/s']:.0f} GB/s", file=sys.stderr, flush=True)

@@ -74,6 +74,10 @@ extern "C" {
 #define RA_SEQ2HEAD 0
 #define RA_HEAD2SEQ 1
 
+/* token grouping of ra_ulysses_pieces tensors */
+#define RA_GROUP_HEADS 0 /* tensor [B, s_loc, P_u runs]: piece j = run j */
+#define RA_GROUP_SEQ 1   /* tensor [B, P_u blocks of s_loc tokens]: piece u = block u */
+
 /* classes of a (query span, key span) pair */
 #define RA_CLASS_SKIP 0 /* no pair visible                               */
 #define RA_CLASS_FULL 1 /* every pair visible                            */
@@ -217,6 +221,29 @@ int ra_rank_backward(const ra_rank_desc* d, const void* q_local,
 int ra_ulysses_relayout(int32_t dir, int32_t elem_bytes, int32_t B,
                         int64_t s_loc, int32_t H, int32_t D, int32_t P_u,
                         const void* in, void* out, void* stream);
+
+/*
+ * ra_ulysses_pieces -- the messages of one Ulysses all-to-all, for up to 4
+ * tensors in one launch ("Sequence Parallelism II": all heads of a rank's
+ * tokens become all tokens of a head subset; ringmaster's Ulysses leg sends
+ * K and V in one collective, its "Status" row 7 fuses Q, K and V).
+ * A piece is the message between one pair of ranks: the n tensors' sections
+ * one after another, section i being [B, s_loc, run_bytes[i]] (a run is the
+ * bytes of one token that go to one destination).  pieces is [P_u, piece],
+ * piece = sum_i B * s_loc * run_bytes[i] bytes.
+ *   RA_GROUP_HEADS (the sender's pack, and the inverse unpack of the returned
+ *     outputs): tensors[i] is [B, s_loc, P_u * run_bytes[i]], and piece j
+ *     section i holds bytes [j run, (j+1) run) of every token (head block j).
+ *   RA_GROUP_SEQ (the receiver's side): tensors[i] is
+ *     [B, P_u * s_loc, run_bytes[i]] in global token order, and piece u
+ *     section i holds tokens [u s_loc, (u+1) s_loc) (those of source u).
+ * to_pieces = 1: tensors -> pieces; 0: pieces -> tensors.  A bit-exact
+ * permutation.  Requires 1 <= n <= 4, P_u >= 1, run_bytes[i] >= 1, pieces
+ * overlapping no tensor, and fewer than 2^31 moved units per tensor.
+ */
+int ra_ulysses_pieces(int32_t to_pieces, int32_t group, int32_t B, int64_t s_loc,
+                      int32_t P_u, int32_t n, void* const* tensors,
+                      const int64_t* run_bytes, void* pieces, void* stream);
 
 /* Host-side plan of one ring step (integers only, no GPU work). */
 typedef struct ra_plan_out {

@@ -23,6 +23,7 @@ RA_DTYPE_F32, RA_DTYPE_BF16 = 0, 1
 RA_ORDER_CONTIGUOUS, RA_ORDER_ZIGZAG = 0, 1
 RA_STEP_INIT, RA_STEP_ACCUM = 0, 1
 RA_SEQ2HEAD, RA_HEAD2SEQ = 0, 1
+RA_GROUP_HEADS, RA_GROUP_SEQ = 0, 1
 RA_CLASS_SKIP, RA_CLASS_FULL, RA_CLASS_DIAG = 0, 1, 2
 CLASS_NAMES = {RA_CLASS_SKIP: "SKIP", RA_CLASS_FULL: "FULL", RA_CLASS_DIAG: "DIAG"}
 ORDERS = {"contiguous": RA_ORDER_CONTIGUOUS, "zigzag": RA_ORDER_ZIGZAG}
@@ -81,17 +82,19 @@ lib.ra_allgather_forward.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp
 lib.ra_rank_backward.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp, _fp, _fp, _vp, _fp, _fp, _fp,
                                  _fp, _vp]
 lib.ra_ulysses_relayout.argtypes = [_i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp]
+lib.ra_ulysses_pieces.argtypes = [_i32, _i32, _i32, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_void_p),
+                                  ctypes.POINTER(ctypes.c_int64), _vp, _vp]
 lib.ra_plan.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ra_plan_out)]
 lib.ra_last_error.restype = ctypes.c_char_p
 lib.ra_last_error.argtypes = []
 lib.ra_abi_version.restype = ctypes.c_int
 lib.ra_abi_version.argtypes = []
 for _f in ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_allgather_forward", "ra_rank_backward",
-           "ra_ulysses_relayout", "ra_plan"):
+           "ra_ulysses_relayout", "ra_ulysses_pieces", "ra_plan"):
     getattr(lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_allgather_forward", "ra_rank_backward",
-           "ra_ulysses_relayout", "ra_plan",
+           "ra_ulysses_relayout", "ra_ulysses_pieces", "ra_plan",
            "ra_last_error", "ra_abi_version")
 
 
@@ -314,6 +317,48 @@ def ra_ulysses_relayout(x, out, P_u: int, direction: int = RA_SEQ2HEAD, *, strea
         raise ValueError(f"out must have shape {want}")
     _check(lib.ra_ulysses_relayout(direction, x.element_size(), B, s_loc, H, D, P_u, _ptr(x),
                                    _ptr(out), _stream(stream)))
+
+
+def ra_ulysses_pieces(tensors, pieces, P_u: int, *, to_pieces: bool, group: int, stream=None) -> None:
+    """Messages of one Ulysses all-to-all for up to 4 tensors in one launch.
+
+    group RA_GROUP_HEADS: tensors [B, s_loc, H_i, D_i] (any dtype); piece j
+    section i is [B, s_loc, H_i/P_u, D_i] (head block j).  group RA_GROUP_SEQ:
+    tensors [B, P_u*s_loc, Hp_i, D_i]; piece u section i is [B, s_loc, Hp_i,
+    D_i] (token block u).  pieces: a contiguous buffer of P_u pieces (bytes
+    in any dtype).  to_pieces selects the direction."""
+    if not 1 <= len(tensors) <= 4:
+        raise ValueError("1 to 4 tensors")
+    t0 = tensors[0]
+    B = t0.shape[0]
+    runs = []
+    for t in tensors:
+        _require(t, "tensor", ndim=4)
+        if t.shape[0] != B:
+            raise ValueError("tensors must share the batch dimension")
+        per_token = t.shape[2] * t.shape[3] * t.element_size()
+        if group == RA_GROUP_HEADS:
+            if t.shape[2] % P_u:
+                raise ValueError("heads must be divisible by P_u")
+            runs.append(per_token // P_u)
+        else:
+            runs.append(per_token)
+    n_tok = t0.shape[1]
+    if any(t.shape[1] != n_tok for t in tensors):
+        raise ValueError("tensors must share the token dimension")
+    if group == RA_GROUP_SEQ:
+        if n_tok % P_u:
+            raise ValueError("tokens must be divisible by P_u")
+        s_loc = n_tok // P_u
+    else:
+        s_loc = n_tok
+    need = P_u * B * s_loc * sum(runs)
+    if not pieces.is_contiguous() or pieces.numel() * pieces.element_size() != need:
+        raise ValueError(f"pieces must be a contiguous buffer of {need} bytes")
+    ptrs = (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+    rb = (ctypes.c_int64 * len(tensors))(*runs)
+    _check(lib.ra_ulysses_pieces(1 if to_pieces else 0, group, B, s_loc, P_u, len(tensors), ptrs, rb,
+                                 _ptr(pieces), _stream(stream)))
 
 
 def ra_plan(order: str, S: int, P: int, rank: int, step: int, causal: bool, tile_q: int,

@@ -133,6 +133,76 @@ hipError_t launch_relayout_w(int dir, uint32_t total, uint32_t units_per_run, in
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Messages of the Ulysses all-to-all for several tensors at once (the fused
+// exchange of ringmaster's Ulysses leg, one collective for K and V, and the
+// receive side of "Sequence Parallelism II").  A piece is the message of one
+// (source, destination) pair: the tensors' sections one after another, each
+// [B, s_loc, run].  Grouping HEADS: tensor i is [B, s_loc, P_u, run_i] and
+// piece j holds run j of every token.  Grouping SEQ: tensor i is
+// [B, P_u, s_loc, run_i] (global token order, block u from source u) and
+// piece u holds block u.  blockIdx.y picks the tensor; threads walk the
+// destination in order (coalesced stores), one W-byte unit each.
+struct PieceSec {
+  const char* src;       // tensor or pieces, by direction
+  char* dst;
+  uint32_t total;        // units of this tensor
+  uint32_t sec;          // units before this section in a piece
+  FastDiv run;           // units per run
+};
+
+struct PieceArgs {
+  PieceSec s[kMaxPieceTensors];
+  uint32_t piece;        // units per piece
+  FastDiv s_loc, pu, bdim;
+  int group, to_pieces;
+};
+
+template <typename W>
+__global__ __launch_bounds__(256) void pieces_kernel(PieceArgs a) {
+  const PieceSec sc = a.s[blockIdx.y];
+  const uint32_t u = blockIdx.x * 256u + threadIdx.x;
+  if (u >= sc.total) return;
+  const uint32_t r = fdiv(u, sc.run);  // run index in destination order
+  const uint32_t e = u - r * sc.run.d;
+  uint32_t j, b, t;
+  if (a.to_pieces) {
+    // destination order (j, b, t)
+    const uint32_t jb = fdiv(r, a.s_loc);
+    t = r - jb * a.s_loc.d;
+    j = fdiv(jb, a.bdim);
+    b = jb - j * a.bdim.d;
+  } else if (a.group == 0) {
+    // tensor order (b, t, j)
+    const uint32_t bt = fdiv(r, a.pu);
+    j = r - bt * a.pu.d;
+    b = fdiv(bt, a.s_loc);
+    t = bt - b * a.s_loc.d;
+  } else {
+    // tensor order (b, j, t)
+    const uint32_t bj = fdiv(r, a.s_loc);
+    t = r - bj * a.s_loc.d;
+    b = fdiv(bj, a.pu);
+    j = bj - b * a.pu.d;
+  }
+  const long long piece_u = (long long)j * a.piece + sc.sec + ((long long)b * a.s_loc.d + t) * sc.run.d + e;
+  const long long tensor_r = a.group == 0 ? ((long long)b * a.s_loc.d + t) * a.pu.d + j
+                                          : ((long long)b * a.pu.d + j) * a.s_loc.d + t;
+  const long long tensor_u = tensor_r * sc.run.d + e;
+  // the destination index is u itself except for pieces, whose sections
+  // interleave
+  const long long src = a.to_pieces ? tensor_u : piece_u;
+  const long long dst = a.to_pieces ? piece_u : (long long)u;
+  ((W*)sc.dst)[dst] = ((const W*)sc.src)[src];
+}
+
+template <typename W>
+hipError_t launch_pieces_w(const PieceArgs& a, int n, uint32_t max_total, hipStream_t s) {
+  const dim3 grid((max_total + 255u) / 256u, (unsigned)n);
+  hipLaunchKernelGGL(pieces_kernel<W>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_lse_merge(long long rows, int D, const float* o_a, const float* lse_a,
@@ -171,6 +241,40 @@ hipError_t launch_relayout(int dir, int elem_bytes, int B, long long s_loc, int 
     case 4: return launch_relayout_w<uint32_t>(dir, total, upr, B, s_loc, P_u, in, out, s);
     case 2: return launch_relayout_w<uint16_t>(dir, total, upr, B, s_loc, P_u, in, out, s);
     default: return launch_relayout_w<uint8_t>(dir, total, upr, B, s_loc, P_u, in, out, s);
+  }
+}
+
+hipError_t launch_pieces(int to_pieces, int group, int B, long long s_loc, int P_u, int n, void* const* tensors,
+                         const long long* run_bytes, void* pieces, int unit, hipStream_t s) {
+  PieceArgs a = {};
+  long long sec = 0, piece = 0;
+  for (int i = 0; i < n; ++i) piece += (long long)B * s_loc * run_bytes[i];
+  uint32_t max_total = 0;
+  for (int i = 0; i < n; ++i) {
+    const uint32_t run = (uint32_t)(run_bytes[i] / unit);
+    const uint32_t total = (uint32_t)((long long)P_u * B * s_loc * run);
+    char* piece_base = (char*)pieces;
+    a.s[i].src = to_pieces ? (const char*)tensors[i] : (const char*)piece_base;
+    a.s[i].dst = to_pieces ? piece_base : (char*)tensors[i];
+    a.s[i].total = total;
+    a.s[i].sec = (uint32_t)(sec / unit);
+    a.s[i].run = make_fastdiv(run);
+    sec += (long long)B * s_loc * run_bytes[i];
+    if (total > max_total) max_total = total;
+  }
+  a.piece = (uint32_t)(piece / unit);
+  a.s_loc = make_fastdiv((uint32_t)s_loc);
+  a.pu = make_fastdiv((uint32_t)P_u);
+  a.bdim = make_fastdiv((uint32_t)B);
+  a.group = group;
+  a.to_pieces = to_pieces;
+  if (max_total == 0) return hipSuccess;
+  switch (unit) {
+    case 16: return launch_pieces_w<uint4>(a, n, max_total, s);
+    case 8: return launch_pieces_w<uint2>(a, n, max_total, s);
+    case 4: return launch_pieces_w<uint32_t>(a, n, max_total, s);
+    case 2: return launch_pieces_w<uint16_t>(a, n, max_total, s);
+    default: return launch_pieces_w<uint8_t>(a, n, max_total, s);
   }
 }
 

@@ -437,4 +437,42 @@ int ra_ulysses_relayout(int32_t dir, int32_t elem_bytes, int32_t B, int64_t s_lo
   return ok();
 }
 
+int ra_ulysses_pieces(int32_t to_pieces, int32_t group, int32_t B, int64_t s_loc, int32_t P_u, int32_t n,
+                      void* const* tensors, const int64_t* run_bytes, void* pieces, void* stream) {
+  if (to_pieces != 0 && to_pieces != 1) return fail(RA_E_INVAL, "to_pieces must be 0 or 1");
+  if (group != RA_GROUP_HEADS && group != RA_GROUP_SEQ)
+    return fail(RA_E_INVAL, "group must be RA_GROUP_HEADS or RA_GROUP_SEQ");
+  if (n < 1 || n > ra::kMaxPieceTensors) return fail(RA_E_INVAL, "n = %d outside [1, %d]", n, ra::kMaxPieceTensors);
+  if (B < 0 || s_loc < 0 || P_u < 1) return fail(RA_E_INVAL, "bad shape");
+  if (!tensors || !run_bytes) return fail(RA_E_INVAL, "NULL tensor or run list");
+  int64_t piece = 0;
+  for (int i = 0; i < n; ++i) {
+    if (run_bytes[i] < 1) return fail(RA_E_INVAL, "run_bytes[%d] must be >= 1", i);
+    piece += (int64_t)B * s_loc * run_bytes[i];
+  }
+  if (piece == 0) return ok();
+  if (!pieces) return fail(RA_E_INVAL, "NULL pieces");
+  const uintptr_t p0 = (uintptr_t)pieces, p1 = p0 + (uintptr_t)(piece * P_u);
+  uintptr_t align = p0 | (uintptr_t)piece;
+  int64_t sec = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!tensors[i]) return fail(RA_E_INVAL, "NULL tensor %d", i);
+    const int64_t bytes = (int64_t)P_u * B * s_loc * run_bytes[i];
+    const uintptr_t t0 = (uintptr_t)tensors[i], t1 = t0 + (uintptr_t)bytes;
+    if (t0 < p1 && p0 < t1) return fail(RA_E_INVAL, "tensor %d overlaps the pieces", i);
+    align |= t0 | (uintptr_t)run_bytes[i] | (uintptr_t)sec;
+    sec += (int64_t)B * s_loc * run_bytes[i];
+  }
+  int unit = 16;
+  while (unit > 1 && (align % (uintptr_t)unit)) unit /= 2;
+  for (int i = 0; i < n; ++i)
+    if ((int64_t)P_u * B * s_loc * (run_bytes[i] / unit) >= ((int64_t)1 << 31))
+      return fail(RA_E_INVAL, "tensor %d too large for one call (2^31 units)", i);
+  if (piece * P_u / unit >= ((int64_t)1 << 31)) return fail(RA_E_INVAL, "pieces too large for one call");
+  hipError_t e = ra::launch_pieces(to_pieces, group, B, s_loc, P_u, n, tensors, (const long long*)run_bytes, pieces,
+                                   unit, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RA_E_HIP, "pieces launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

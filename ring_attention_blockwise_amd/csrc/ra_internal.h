@@ -86,4 +86,12 @@ hipError_t launch_relayout(int dir, int elem_bytes, int B, long long s_loc,
                            int H, int D, int P_u, const void* in, void* out,
                            hipStream_t s);
 
+// Multi-tensor Ulysses messages (at most kMaxPieceTensors tensors per call).
+// to_pieces: tensors -> pieces, else pieces -> tensors; group 0: head blocks,
+// 1: token blocks; unit: bytes moved per thread (divides every run, section
+// and pointer).
+constexpr int kMaxPieceTensors = 4;
+hipError_t launch_pieces(int to_pieces, int group, int B, long long s_loc, int P_u, int n, void* const* tensors,
+                         const long long* run_bytes, void* pieces, int unit, hipStream_t s);
+
 }  // namespace ra

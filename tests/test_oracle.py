@@ -385,3 +385,51 @@ def test_relayout_matches_reshape_and_round_trips(P_u):
     ref = x.reshape(B, s_loc, P_u, H // P_u, D).transpose(2, 0, 1, 3, 4)
     np.testing.assert_array_equal(y, ref)
     np.testing.assert_array_equal(orl.head2seq(y), x)
+
+
+# ---------------------------------------------------------------------------
+# Multi-tensor Ulysses messages
+
+def test_pieces_one_tensor_heads_is_seq2head():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((2, 5, 8, 3)).astype(np.float32)
+    from oracle import relayout as rl
+    pcs = rl.to_pieces([x], 4, "heads")
+    np.testing.assert_array_equal(np.stack([p[0] for p in pcs]), rl.seq2head(x, 4))
+    np.testing.assert_array_equal(rl.piece_bytes(pcs), np.ascontiguousarray(rl.seq2head(x, 4)).view(np.uint8).ravel())
+
+
+@pytest.mark.parametrize("group", ["heads", "seq"])
+def test_pieces_round_trip(group):
+    from oracle import relayout as rl
+    rng = np.random.default_rng(22)
+    xs = [rng.standard_normal((2, 12, 6, 4)).astype(np.float32),
+          rng.integers(0, 65535, (2, 12, 3, 8), dtype=np.uint16)]
+    back = rl.from_pieces(rl.to_pieces(xs, 3, group), group)
+    for a, b in zip(xs, back):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_ulysses_exchange_gives_each_rank_all_tokens_of_its_heads():
+    """Sequence Parallelism II: before the all-to-all rank u holds all heads
+    of tokens [u s, (u+1) s); after it rank j holds all tokens of head block
+    j.  Pack, exchange and the receiver's regrouping must give exactly the
+    global tensor's head block, and the way back must restore the shards."""
+    from oracle import relayout as rl
+    rng = np.random.default_rng(23)
+    P_u, B, S = 4, 2, 16
+    Q = rng.standard_normal((B, S, 8, 5))
+    K = rng.standard_normal((B, S, 4, 5))
+    s_loc = S // P_u
+    shards = [[Q[:, u * s_loc:(u + 1) * s_loc], K[:, u * s_loc:(u + 1) * s_loc]] for u in range(P_u)]
+    recv = rl.exchange([rl.to_pieces(sh, P_u, "heads") for sh in shards])
+    for j in range(P_u):
+        q_j, k_j = rl.from_pieces(recv[j], "seq")
+        np.testing.assert_array_equal(q_j, Q[:, :, 2 * j:2 * j + 2])
+        np.testing.assert_array_equal(k_j, K[:, :, j:j + 1])
+    # the way back (outputs of the head blocks to their token owners)
+    outs = [[Q[:, :, 2 * j:2 * j + 2]] for j in range(P_u)]
+    back = rl.exchange([rl.to_pieces(o, P_u, "seq") for o in outs])
+    for u in range(P_u):
+        (o_u,) = rl.from_pieces(back[u], "heads")
+        np.testing.assert_array_equal(o_u, Q[:, u * s_loc:(u + 1) * s_loc])
