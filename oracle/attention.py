@@ -32,11 +32,12 @@ from . import index_maps as im
 ROW_BLOCK = 256
 
 
-def attention_rows(q, qpos, k, v, kpos, causal: bool, scale: float):
+def attention_rows(q, qpos, k, v, kpos, causal: bool, scale: float, window: int = 0, cu_seqlens=None):
     """Attention of query rows over a set of key rows.
 
     q: [B, Nq, Hq, D]; k, v: [B, Nk, Hkv, D] (any float dtype, computed in
-    float64); qpos [Nq] and kpos [Nk] are global positions.  Returns
+    float64); qpos [Nq] and kpos [Nk] are global positions; ``window`` and
+    ``cu_seqlens`` select the mask variants of ``index_maps.visible_masked``.  Returns
     O [B, Nq, Hq, D] and LSE [B, Nq, Hq] (float64).  With the keys of the whole
     sequence this is the definition; with the keys of one shard it is that
     shard's partial result.
@@ -61,7 +62,8 @@ def attention_rows(q, qpos, k, v, kpos, causal: bool, scale: float):
             for r0 in range(0, Nq, ROW_BLOCK):
                 r1 = min(Nq, r0 + ROW_BLOCK)
                 pos = qpos[r0:r1]
-                vis = im.visible(pos, kpos, causal)
+                vis = (im.visible(pos, kpos, causal) if not window and cu_seqlens is None
+                       else im.visible_masked(pos, kpos, causal, window, cu_seqlens))
                 # keys no query of this row block can see carry zero weight
                 keep = vis.any(axis=0)
                 if not keep.any():

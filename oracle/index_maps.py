@@ -85,6 +85,32 @@ def visible(qpos: np.ndarray, kpos: np.ndarray, causal: bool) -> np.ndarray:
     return kpos[None, :] <= qpos[:, None]
 
 
+def segment_ids(pos, cu_seqlens) -> np.ndarray:
+    """Index of the packed sequence holding each position: sequence i covers
+    [cu_seqlens[i], cu_seqlens[i+1])."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    return np.searchsorted(cu, np.asarray(pos, dtype=np.int64), side="right") - 1
+
+
+def visible_masked(qpos, kpos, causal: bool, window: int = 0, cu_seqlens=None) -> np.ndarray:
+    """Visibility with the mask variants the tile classifier extends to.
+
+    ringmaster names them only ("Status": sliding-window attention through the
+    kernel's window, and packing / varlen).  Readings: a window w > 0 (with
+    the causal mask) lets query t see the w most recent keys t-w+1 .. t; packed
+    sequences (boundaries 0 = c_0 < c_1 < ... < c_n = S) let a query see only
+    keys of its own sequence, under the causal (and window) rule if set.
+    """
+    qpos = np.asarray(qpos, dtype=np.int64)
+    kpos = np.asarray(kpos, dtype=np.int64)
+    v = visible(qpos, kpos, causal)
+    if window:
+        v = v & ((qpos[:, None] - kpos[None, :]) < window)
+    if cu_seqlens is not None:
+        v = v & (segment_ids(qpos, cu_seqlens)[:, None] == segment_ids(kpos, cu_seqlens)[None, :])
+    return v
+
+
 def block_class_bruteforce(qpos, kpos, causal: bool) -> str:
     """Class of a block by enumerating every (query, key) pair."""
     v = visible(qpos, kpos, causal)

@@ -433,3 +433,74 @@ def test_ulysses_exchange_gives_each_rank_all_tokens_of_its_heads():
     for u in range(P_u):
         (o_u,) = rl.from_pieces(back[u], "heads")
         np.testing.assert_array_equal(o_u, Q[:, u * s_loc:(u + 1) * s_loc])
+
+
+# ---------------------------------------------------------------------------
+# Mask variants: sliding window and packed sequences
+
+def _brute_visible(qpos, kpos, causal, window, cu):
+    out = np.zeros((len(qpos), len(kpos)), dtype=bool)
+    for a, t in enumerate(qpos):
+        st = max(c for c in cu[:-1] if c <= t) if cu is not None else None
+        for b, j in enumerate(kpos):
+            ok = (not causal) or j <= t
+            if window:
+                ok = ok and t - j < window
+            if cu is not None:
+                sj = max(c for c in cu[:-1] if c <= j)
+                ok = ok and sj == st
+            out[a, b] = ok
+    return out
+
+
+@pytest.mark.parametrize("causal,window,cu", [
+    (True, 5, None), (True, 1, None), (True, 0, [0, 7, 9, 20, 32]), (False, 0, [0, 3, 32]),
+    (True, 4, [0, 11, 12, 30, 32]),
+])
+def test_masked_visibility_matches_enumeration(causal, window, cu):
+    pos = np.arange(32)
+    rng = np.random.default_rng(8)
+    qpos = rng.permutation(pos)[:20]
+    np.testing.assert_array_equal(im.visible_masked(qpos, pos, causal, window, cu),
+                                  _brute_visible(qpos, pos, causal, window, cu))
+
+
+def test_window_of_one_returns_own_value():
+    """Window 1: each query sees only itself, so O_t = V_t and LSE_t = s_tt."""
+    rng = np.random.default_rng(9)
+    B, S, H, D = 1, 12, 2, 4
+    Q, K, V = (rng.standard_normal((B, S, H, D)) for _ in range(3))
+    pos = np.arange(S)
+    o, lse = oa.attention_rows(Q, pos, K, V, pos, True, 0.7, window=1)
+    np.testing.assert_allclose(o, V, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, 0.7 * (Q * K).sum(-1), rtol=0, atol=1e-14)
+
+
+def test_full_window_and_single_sequence_are_the_causal_mask():
+    rng = np.random.default_rng(10)
+    B, S, H, D = 1, 24, 2, 4
+    Q, K, V = (rng.standard_normal((B, S, H, D)) for _ in range(3))
+    pos = np.arange(S)
+    ref = oa.attention_rows(Q, pos, K, V, pos, True, 0.5)
+    for kw in (dict(window=S), dict(cu_seqlens=[0, S])):
+        o, lse = oa.attention_rows(Q, pos, K, V, pos, True, 0.5, **kw)
+        np.testing.assert_allclose(o, ref[0], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse, ref[1], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_packed_sequences_are_independent(causal):
+    """Packing is only a layout: each sequence of the pack gives what it gives
+    alone (plain attention over its own tokens)."""
+    rng = np.random.default_rng(11)
+    B, H, D = 2, 2, 4
+    cu = [0, 5, 6, 19, 30]
+    S = cu[-1]
+    Q, K, V = (rng.standard_normal((B, S, H, D)) for _ in range(3))
+    pos = np.arange(S)
+    o, lse = oa.attention_rows(Q, pos, K, V, pos, causal, 0.6, cu_seqlens=cu)
+    for a, b in zip(cu[:-1], cu[1:]):
+        p = np.arange(b - a)
+        o_s, l_s = oa.attention_rows(Q[:, a:b], p, K[:, a:b], V[:, a:b], p, causal, 0.6)
+        np.testing.assert_allclose(o[:, a:b], o_s, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[:, a:b], l_s, rtol=0, atol=1e-13)
