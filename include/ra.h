@@ -160,6 +160,32 @@ int ra_rank_forward(const ra_rank_desc* d, const void* q_local,
                     const void* k_shards, const void* v_shards, float* o,
                     float* lse, void* stream);
 
+/* Mask variants of the tile classifier (ringmaster "Status": sliding-window
+ * attention through the kernel's window; packing / varlen).  Readings: a
+ * window w > 0 (with the causal mask) lets query t see keys t-w+1 .. t;
+ * packed sequences with boundaries 0 = c_0 < c_1 < ... < c_n = S let a query
+ * see only keys of its own sequence (under the causal rule, and the window,
+ * if set). */
+typedef struct ra_mask {
+  int64_t window;               /* 0: no window; > 0 requires causal         */
+  int32_t n_seqs;               /* packed sequences: count, or 0 (none)      */
+  const int64_t* cu_seqlens;    /* host copy of the n_seqs + 1 boundaries    */
+  const int64_t* cu_seqlens_dev;/* the same values in device memory          */
+} ra_mask;
+
+/*
+ * ra_rank_forward_masked -- ra_rank_forward with a sliding window and/or
+ * packed sequences.  Tiles the mask hides are not visited; a step whose
+ * whole block is hidden is not launched; rows with no visible key in a step
+ * keep the merge identity.  m == NULL is ra_rank_forward.  bf16 only
+ * (RA_E_UNSUPPORTED for float32 inputs with a mask).  Both copies of the
+ * boundaries must stay unchanged until the work completes.
+ */
+int ra_rank_forward_masked(const ra_rank_desc* d, const ra_mask* m,
+                           const void* q_local, const void* k_shards,
+                           const void* v_shards, float* o, float* lse,
+                           void* stream);
+
 /*
  * ra_allgather_forward -- the all-gather form of the same rank's attention:
  * every key/value token is resident at once, so the rank's queries attend to

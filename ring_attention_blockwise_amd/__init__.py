@@ -54,6 +54,11 @@ class ra_rank_desc(ctypes.Structure):
                 ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
+class ra_mask(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int64), ("n_seqs", ctypes.c_int32),
+                ("cu_seqlens", ctypes.POINTER(ctypes.c_int64)), ("cu_seqlens_dev", ctypes.c_void_p)]
+
+
 class ra_plan_out(ctypes.Structure):
     _fields_ = [("src", ctypes.c_int32), ("n_qspans", ctypes.c_int32), ("n_kspans", ctypes.c_int32),
                 ("qspans", ra_span * 2), ("kspans", ra_span * 2),
@@ -79,6 +84,8 @@ lib.ra_step.argtypes = [ctypes.POINTER(ra_step_desc), _vp, _vp, _vp, _fp, _fp, _
 lib.ra_lse_merge.argtypes = [_i64, _i32, _fp, _fp, _fp, _fp, _fp, _fp, _vp]
 lib.ra_rank_forward.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp, _fp, _fp, _vp]
 lib.ra_allgather_forward.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp, _fp, _fp, _vp]
+lib.ra_rank_forward_masked.argtypes = [ctypes.POINTER(ra_rank_desc), ctypes.POINTER(ra_mask), _vp, _vp, _vp,
+                                       _fp, _fp, _vp]
 lib.ra_rank_backward.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp, _fp, _fp, _vp, _fp, _fp, _fp,
                                  _fp, _vp]
 lib.ra_ulysses_relayout.argtypes = [_i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp]
@@ -89,11 +96,13 @@ lib.ra_last_error.restype = ctypes.c_char_p
 lib.ra_last_error.argtypes = []
 lib.ra_abi_version.restype = ctypes.c_int
 lib.ra_abi_version.argtypes = []
-for _f in ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_allgather_forward", "ra_rank_backward",
+for _f in ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_rank_forward_masked", "ra_allgather_forward",
+           "ra_rank_backward",
            "ra_ulysses_relayout", "ra_ulysses_pieces", "ra_plan"):
     getattr(lib, _f).restype = ctypes.c_int
 
-EXPORTS = ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_allgather_forward", "ra_rank_backward",
+EXPORTS = ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_rank_forward_masked", "ra_allgather_forward",
+           "ra_rank_backward",
            "ra_ulysses_relayout", "ra_ulysses_pieces", "ra_plan",
            "ra_last_error", "ra_abi_version")
 
@@ -216,6 +225,44 @@ def ra_rank_forward(q_local, k_shards, v_shards, o, lse, *, S: int, P: int, rank
                      1 if causal else 0, float(scale if scale is not None else D ** -0.5))
     _check(lib.ra_rank_forward(ctypes.byref(d), _ptr(q_local), _ptr(k_shards), _ptr(v_shards),
                                _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def ra_rank_forward_masked(q_local, k_shards, v_shards, o, lse, *, S: int, P: int, rank: int, order: str,
+                           causal: bool, scale: float | None = None, window: int = 0, cu_seqlens=None,
+                           stream=None) -> None:
+    """ra_rank_forward with a sliding window (``window`` > 0, causal) and/or
+    packed sequences (``cu_seqlens``: boundaries 0 = c_0 < ... < c_n = S, a
+    sequence of ints).  bf16 inputs."""
+    torch = _torch()
+    _require(q_local, "q_local", ndim=4)
+    _require(k_shards, "k_shards", dtype=q_local.dtype, ndim=5)
+    _require(v_shards, "v_shards", dtype=q_local.dtype, ndim=5)
+    _require(o, "o", dtype=torch.float32, ndim=4)
+    _require(lse, "lse", dtype=torch.float32, ndim=3)
+    B, s_loc, Hq, D = q_local.shape
+    Hkv = k_shards.shape[3]
+    if P * s_loc != S:
+        raise ValueError("q_local must hold S/P rows")
+    if tuple(k_shards.shape) != (P, B, s_loc, Hkv, D) or k_shards.shape != v_shards.shape:
+        raise ValueError("k_shards and v_shards must be [P, B, S/P, Hkv, D]")
+    if tuple(o.shape) != (B, s_loc, Hq, D) or tuple(lse.shape) != (B, s_loc, Hq):
+        raise ValueError("o must be [B, S/P, Hq, D] and lse [B, S/P, Hq]")
+    d = ra_rank_desc(_dtype_code(q_local), B, Hq, Hkv, D, S, P, rank, ORDERS[order],
+                     1 if causal else 0, float(scale if scale is not None else D ** -0.5))
+    host = dev = None
+    n = 0
+    if cu_seqlens is not None:
+        cu = [int(c) for c in cu_seqlens]
+        n = len(cu) - 1
+        host = (ctypes.c_int64 * len(cu))(*cu)
+        # allocated on the launch stream, so the stream-ordered allocator keeps
+        # it for the kernels enqueued below
+        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+            dev = torch.tensor(cu, dtype=torch.int64, device="cuda")
+    m = ra_mask(int(window), n, ctypes.cast(host, ctypes.POINTER(ctypes.c_int64)) if host is not None else None,
+                dev.data_ptr() if dev is not None else None)
+    _check(lib.ra_rank_forward_masked(ctypes.byref(d), ctypes.byref(m), _ptr(q_local), _ptr(k_shards),
+                                      _ptr(v_shards), _ptr(o), _ptr(lse), _stream(stream)))
 
 
 def ra_allgather_forward(q_local, k_global, v_global, o, lse, *, S: int, P: int, rank: int, order: str,

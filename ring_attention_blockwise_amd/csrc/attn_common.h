@@ -61,14 +61,20 @@ struct KTile {
 };
 
 struct TilePlan {
-  int nf[2], nr[2];    // full and masked tiles per span
-  long long hi[2];     // keys of the span visible to the work item's last row
+  // Per key span, in tiles of kBK keys counted from the span's first key:
+  // unmasked tiles [fb, fb + nf), masked tiles below them [lb, lb + nlo)
+  // (a sliding window's or a packed sequence's left edge) and above them
+  // [hb, hb + nr) (the causal diagonal, a span's ragged end).
+  int fb[2], nf[2], lb[2], nlo[2], hb[2], nr[2];
+  long long hi[2];     // keys of the span visible to some row of the work item: [0, hi)
   long long off[2];    // first local row of each key span
   long long start[2];  // its global position
   int n_full, n;
 
-  // Only selects between the two spans: no indexing by a run-time span
-  // number, which would re-read the kernel arguments on every tile.
+  // Tile t in plan order, for plans without masked tiles below the unmasked
+  // ones (no window, no packed sequences).  Only selects between the two
+  // spans: no indexing by a run-time span number, which would re-read the
+  // kernel arguments on every tile.
   __device__ KTile tile(int t) const {
     bool s1;
     long long kin;
@@ -88,30 +94,77 @@ struct TilePlan {
   }
 };
 
+// Packed sequences: boundaries cu[0] = 0 < cu[1] < ... < cu[nseg] (global
+// positions).  Index of the sequence holding t.
+__device__ inline int seg_of(const StepParams& p, long long t) {
+  int lo = 0, hi = p.nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.cu[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Keys visible to the query at global position t: [key_lo(t), key_hi(t)].
+// Both are non-decreasing in t, so a run of rows r0..r1 sees keys
+// [key_lo(r0), key_hi(r1)] and every one of them sees [key_lo(r1), key_hi(r0)].
+__device__ inline long long key_lo(const StepParams& p, long long t) {
+  long long lo = p.window > 0 ? t - p.window + 1 : 0;
+  if (p.cu) lo = max(lo, p.cu[seg_of(p, t)]);
+  return lo;
+}
+__device__ inline long long key_hi(const StepParams& p, long long t) {
+  if (p.causal) return t;
+  if (p.cu) return p.cu[seg_of(p, t) + 1] - 1;
+  return 0x3fffffffffffffffLL;
+}
+
 __device__ inline TilePlan plan_tiles(const StepParams& p, long long qglob0, long long qglob_last) {
   TilePlan tp;
   tp.n_full = 0;
   tp.n = 0;
+  const long long lo0 = key_lo(p, qglob0), lo1 = key_lo(p, qglob_last);
+  const long long hi0 = key_hi(p, qglob0), hi1 = key_hi(p, qglob_last);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    long long hi = 0, full = 0;
+    long long v0 = 0, v1 = 0, f0 = 0, f1 = 0;
     if (s < p.nks) {
-      hi = p.ks_len[s];
-      full = hi;
-      if (p.causal) {
-        hi = min(hi, qglob_last + 1 - p.ks_start[s]);   // keys <= the last row
-        full = min(hi, qglob0 + 1 - p.ks_start[s]);     // keys <= the first row
-      }
-      hi = max(hi, 0LL);
-      full = max(full, 0LL);
+      const long long ks = p.ks_start[s], len = p.ks_len[s];
+      v0 = min(max(lo0 - ks, 0LL), len);
+      v1 = min(max(hi1 - ks + 1, 0LL), len);
+      f0 = min(max(lo1 - ks, 0LL), len);
+      f1 = min(max(hi0 - ks + 1, 0LL), len);
     }
-    tp.hi[s] = hi;
+    int fb = 0, nf = 0, lb = 0, nlo = 0, hb = 0, nr = 0;
+    if (v1 > v0) {
+      const int lt = (int)(v0 / kBK), ht = (int)((v1 + kBK - 1) / kBK);
+      const int ff = (int)((f0 + kBK - 1) / kBK), fe = (int)(f1 / kBK);
+      if (fe > ff) {
+        fb = ff;
+        nf = fe - ff;
+        lb = lt;
+        nlo = ff - lt;
+        hb = fe;
+        nr = ht - fe;
+      } else {
+        fb = lt;
+        lb = lt;
+        hb = lt;
+        nr = ht - lt;
+      }
+    }
+    tp.fb[s] = fb;
+    tp.nf[s] = nf;
+    tp.lb[s] = lb;
+    tp.nlo[s] = nlo;
+    tp.hb[s] = hb;
+    tp.nr[s] = nr;
+    tp.hi[s] = v1;
     tp.off[s] = p.ks_off[s];
     tp.start[s] = p.ks_start[s];
-    tp.nf[s] = (int)(full / kBK);
-    tp.nr[s] = (int)((hi - (long long)tp.nf[s] * kBK + kBK - 1) / kBK);
-    tp.n_full += tp.nf[s];
-    tp.n += tp.nf[s] + tp.nr[s];
+    tp.n_full += nf;
+    tp.n += nf + nlo + nr;
   }
   return tp;
 }
@@ -136,6 +189,7 @@ struct TileCursor {
   long long vis;            // rows of the span visible from local0 on
   int rem;                  // tiles left in the segment, this one included
   int seg;                  // 0, 1: unmasked tiles of span 0, 1; 2, 3: masked
+                            // below them; 4, 5: masked above them
 
   __device__ int count() const { return (int)min((long long)kBK, vis); }
   __device__ bool masked() const { return seg >= 2; }
@@ -144,10 +198,19 @@ struct TileCursor {
     // selects only: a run-time index into the plan's arrays would put the
     // plan in scratch memory
     const bool s = j & 1;
-    const int nf = s ? tp.nf[1] : tp.nf[0];
-    const int n = j < 2 ? nf : (s ? tp.nr[1] : tp.nr[0]);
+    int n, t0;
+    if (j < 2) {
+      n = s ? tp.nf[1] : tp.nf[0];
+      t0 = s ? tp.fb[1] : tp.fb[0];
+    } else if (j < 4) {
+      n = s ? tp.nlo[1] : tp.nlo[0];
+      t0 = s ? tp.lb[1] : tp.lb[0];
+    } else {
+      n = s ? tp.nr[1] : tp.nr[0];
+      t0 = s ? tp.hb[1] : tp.hb[0];
+    }
     if (n == 0) return false;
-    const long long kin = j < 2 ? 0 : (long long)nf * kBK;
+    const long long kin = (long long)t0 * kBK;
     local0 = (s ? tp.off[1] : tp.off[0]) + kin;
     glob0 = (s ? tp.start[1] : tp.start[0]) + kin;
     vis = (s ? tp.hi[1] : tp.hi[0]) - kin;
@@ -155,8 +218,11 @@ struct TileCursor {
     seg = j;
     return true;
   }
+  // The segment loops are unrolled so that every enter() sees a constant j:
+  // with a run-time j the compiler turns the selects back into indexing.
   __device__ void first(const TilePlan& tp) {
-    for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int j = 0; j < 6; ++j)
       if (enter(tp, j)) return;
   }
   __device__ void advance(const TilePlan& tp) {
@@ -167,11 +233,11 @@ struct TileCursor {
       vis -= kBK;
       return;
     }
-    for (int j = seg + 1; j < 4; ++j)
-      if (enter(tp, j)) return;
+#pragma unroll
+    for (int j = 1; j < 6; ++j)
+      if (j > seg && enter(tp, j)) return;
   }
 };
-
 
 // ---------------------------------------------------------------------------
 // Work item of a workgroup: BQ consecutive query rows of one (batch, query

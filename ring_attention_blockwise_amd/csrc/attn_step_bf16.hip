@@ -172,10 +172,11 @@ __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "mem
 // Iteration t.  PAR = t mod 2 names the LDS buffers statically: tile t is read
 // from kbuf[PAR] / vbuf[PAR]; tile t+1 is started first, into kbuf[PAR ^ 1] /
 // vbuf[PAR ^ 1].
-template <int D, int PAR>
+template <int D, int PAR, bool kExt>
 __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const TilePlan& tp, const WorkItem& wi,
                                  const Stager<D>& st, TileCursor& cur, int t, RA_LDS char* const* kbuf,
-                                 RA_LDS char* const* vbuf, int lane, int wave) {
+                                 RA_LDS char* const* vbuf, const RA_LDS int* row_lo, const RA_LDS int* row_hi,
+                                 int lane, int wave) {
   const Lane<D> ln((unsigned)(p.Hkv * D * 2), wave);
   const TileCursor ti = cur;
   // Two workgroups share each CU; the wave arbiter favours the older one,
@@ -216,17 +217,21 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
   // the tile is visible to row q iff k < lim(q)
   const int L = lane >> 5;
   if (ti.masked()) {
-    // rows of this wave see keys < (qglob0 - glob0 + 1) + row, clamped so the
-    // sum stays in int range (|row| < 256)
+    // keys of the tile visible to the row: below lim (the causal diagonal, a
+    // span's ragged end, a packed sequence's end) and, with a window or
+    // packed sequences, from lo on.  The sign bit of each distance selects
+    // -inf with a bitfield insert (no compare masks, which would take scalar
+    // registers).
     const long long d0 = wi.qglob0 - ti.glob0 + 1;
     const int dc = p.causal ? (int)max(-1024LL, min(1024LL, d0)) : 1024;
+    const int base = kExt ? (int)max(-(1LL << 30), min(1LL << 30, ti.glob0 - wi.qglob0)) : 0;
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
-      const int lim = min(ti.count(), max(0, dc + 64 * wave + 32 * qb + (lane & 31)));
+      const int ri = 64 * wave + 32 * qb + (lane & 31);
+      int lim = min(ti.count(), max(0, dc + ri));
+      if (kExt) lim = max(0, min(ti.count(), row_hi[ri] + 1 - base));
       // key of register r is 16(r/8) + r%8 + 8L: it is visible iff
-      // lim - 8L - 1 - (16(r/8) + r%8) >= 0.  The sign bit of that difference
-      // selects -inf with a bitfield insert (no compare masks, which would
-      // take scalar registers).
+      // lim - 8L - 1 - (16(r/8) + r%8) >= 0
       const int lim_l = lim - 8 * L - 1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -234,6 +239,21 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
         asm volatile("" : "+v"(d));
         const unsigned m = (unsigned)(d >> 31);
         s[qb][r] = __uint_as_float((m & 0xff800000u) | (~m & __float_as_uint(s[qb][r])));
+      }
+    }
+    if (kExt) {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        const int ri = 64 * wave + 32 * qb + (lane & 31);
+        // visible iff key - lo >= 0
+        const int lo_l = 8 * L - max(-1, min(33, row_lo[ri] - base));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int d = lo_l + (16 * (r >> 3) + (r & 7));
+          asm volatile("" : "+v"(d));
+          const unsigned m = (unsigned)(d >> 31);
+          s[qb][r] = __uint_as_float((m & 0xff800000u) | (~m & __float_as_uint(s[qb][r])));
+        }
       }
     }
   }
@@ -316,7 +336,7 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
   __syncthreads();
 }
 
-template <int D>
+template <int D, bool kExt>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_step_bf16_kernel(StepParams p) {
   typedef Layout<D> Ly;
@@ -326,6 +346,9 @@ void attn_step_bf16_kernel(StepParams p) {
   __shared__ __attribute__((aligned(16))) char v1_raw[Ly::kVTileBytes];
   RA_LDS char* const kbuf[2] = {(RA_LDS char*)k0_raw, (RA_LDS char*)k1_raw};
   RA_LDS char* const vbuf[2] = {(RA_LDS char*)v0_raw, (RA_LDS char*)v1_raw};
+  __shared__ int lo_raw[kBQBf16], hi_raw[kBQBf16];
+  const RA_LDS int* row_lo = (const RA_LDS int*)lo_raw;
+  const RA_LDS int* row_hi = (const RA_LDS int*)hi_raw;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -336,6 +359,16 @@ void attn_step_bf16_kernel(StepParams p) {
   if (tp.n == 0) {
     store_identity<D, kThreads>(p, wi);
     return;
+  }
+
+  if (kExt) {
+    // visible key range of each row of the work item (window, packed
+    // sequences), relative to the item's first row and clamped to +-2^30
+    for (int r = threadIdx.x; r < kBQBf16; r += kThreads) {
+      const long long t = wi.qglob0 + r;
+      lo_raw[r] = (int)max(-(1LL << 30), min(1LL << 30, key_lo(p, t) - wi.qglob0));
+      hi_raw[r] = (int)max(-(1LL << 30), min(1LL << 30, key_hi(p, t) - wi.qglob0));
+    }
   }
 
   // prologue: tile 0 in flight while Q is read
@@ -365,10 +398,10 @@ void attn_step_bf16_kernel(StepParams p) {
   // iteration t uses parity t mod 2.
   int t = 0;
   for (; t + 1 < tp.n; t += 2) {
-    step_tile<D, 0>(ws, p, tp, wi, st, cur, t, kbuf, vbuf, lane, wave);
-    step_tile<D, 1>(ws, p, tp, wi, st, cur, t + 1, kbuf, vbuf, lane, wave);
+    step_tile<D, 0, kExt>(ws, p, tp, wi, st, cur, t, kbuf, vbuf, row_lo, row_hi, lane, wave);
+    step_tile<D, 1, kExt>(ws, p, tp, wi, st, cur, t + 1, kbuf, vbuf, row_lo, row_hi, lane, wave);
   }
-  if (t < tp.n) step_tile<D, 0>(ws, p, tp, wi, st, cur, t, kbuf, vbuf, lane, wave);
+  if (t < tp.n) step_tile<D, 0, kExt>(ws, p, tp, wi, st, cur, t, kbuf, vbuf, row_lo, row_hi, lane, wave);
 
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
@@ -380,7 +413,10 @@ void attn_step_bf16_kernel(StepParams p) {
 
 template <int D>
 hipError_t launch(const StepParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(attn_step_bf16_kernel<D>, dim3(8 * p.per_xcd), dim3(kThreads), 0, s, p);
+  if (p.mask_ext)
+    hipLaunchKernelGGL((attn_step_bf16_kernel<D, true>), dim3(8 * p.per_xcd), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_step_bf16_kernel<D, false>), dim3(8 * p.per_xcd), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

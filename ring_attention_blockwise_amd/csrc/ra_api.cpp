@@ -3,6 +3,7 @@
 // enqueued, so a failing call leaves the caller's buffers untouched.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -77,6 +78,53 @@ int32_t pair_class(int64_t q0, int64_t nq, int64_t k0, int64_t nk, bool causal) 
   return RA_CLASS_DIAG;
 }
 
+// Keys visible to the query at global position t under a mask: [key_lo(t),
+// key_hi(t)], both non-decreasing in t.
+int64_t seq_index(const ra_mask* m, int64_t t) {
+  const int64_t* cu = m->cu_seqlens;
+  int lo = 0, hi = m->n_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (cu[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+int64_t host_key_lo(const ra_mask* m, int64_t t) {
+  int64_t lo = m->window > 0 ? t - m->window + 1 : 0;
+  if (m->n_seqs > 0) lo = std::max(lo, m->cu_seqlens[seq_index(m, t)]);
+  return lo;
+}
+int64_t host_key_hi(const ra_mask* m, bool causal, int64_t t) {
+  if (causal) return t;
+  if (m->n_seqs > 0) return m->cu_seqlens[seq_index(m, t) + 1] - 1;
+  return INT64_MAX;
+}
+// Does some query of [q0, q0+nq) see some key of [k0, k0+nk)?
+bool span_sees(int64_t q0, int64_t nq, int64_t k0, int64_t nk, bool causal, const ra_mask* m) {
+  if (nq <= 0 || nk <= 0) return false;
+  if (!m) return pair_class(q0, nq, k0, nk, causal) != RA_CLASS_SKIP;
+  const int64_t lo = std::max(host_key_lo(m, q0), k0);
+  const int64_t hi = std::min(host_key_hi(m, causal, q0 + nq - 1), k0 + nk - 1);
+  return lo <= hi;
+}
+
+int check_mask(const ra_mask* m, int64_t S, bool causal) {
+  if (!m) return RA_OK;
+  if (m->window < 0) return fail(RA_E_INVAL, "window must be >= 0");
+  if (m->window > 0 && !causal) return fail(RA_E_INVAL, "a window needs the causal mask");
+  if (m->n_seqs < 0) return fail(RA_E_INVAL, "n_seqs must be >= 0");
+  if (m->n_seqs > 0) {
+    if (!m->cu_seqlens || !m->cu_seqlens_dev) return fail(RA_E_INVAL, "cu_seqlens (host and device) must be given");
+    if (!aligned(m->cu_seqlens_dev, 8)) return fail(RA_E_INVAL, "cu_seqlens_dev must be 8-byte aligned");
+    if (m->cu_seqlens[0] != 0 || m->cu_seqlens[m->n_seqs] != S)
+      return fail(RA_E_INVAL, "cu_seqlens must run from 0 to S = %lld", (long long)S);
+    for (int i = 0; i < m->n_seqs; ++i)
+      if (m->cu_seqlens[i + 1] <= m->cu_seqlens[i]) return fail(RA_E_INVAL, "cu_seqlens must increase strictly");
+  }
+  return RA_OK;
+}
+
 // ---------------------------------------------------------------------------
 int check_step(const ra_step_desc* d, const void* q, const void* k, const void* v, const float* o,
                const float* lse, uint32_t flags) {
@@ -120,7 +168,7 @@ int check_step(const ra_step_desc* d, const void* q, const void* k, const void* 
 // Builds the kernel parameters of one step.  Returns false when nothing has to
 // be launched (empty rows, or ACCUM with every pair masked).
 bool build_params(const ra_step_desc* d, const void* q, const void* k, const void* v, float* o,
-                  float* lse, bool accum, ra::StepParams* p) {
+                  float* lse, bool accum, ra::StepParams* p, const ra_mask* m = nullptr) {
   if (d->Sq == 0) return false;
   p->q = q;
   p->k = k;
@@ -137,6 +185,10 @@ bool build_params(const ra_step_desc* d, const void* q, const void* k, const voi
   p->accum = accum ? 1 : 0;
   p->scale = d->scale;
   p->sl2 = (float)((double)d->scale * 1.4426950408889634);
+  p->window = m ? m->window : 0;
+  p->cu = m && m->n_seqs > 0 ? (const long long*)m->cu_seqlens_dev : nullptr;
+  p->nseg = m ? m->n_seqs : 0;
+  p->mask_ext = (p->window > 0 || p->cu) ? 1 : 0;
   p->nks = 0;
   int64_t off = 0;
   for (int i = 0; i < d->n_kspans; ++i) {
@@ -153,8 +205,7 @@ bool build_params(const ra_step_desc* d, const void* q, const void* k, const voi
   for (int i = 0; i < d->n_qspans; ++i) {
     const ra_span qs = d->qspans[i];
     bool any = false;
-    for (int j = 0; j < p->nks; ++j)
-      any |= pair_class(qs.start, qs.len, p->ks_start[j], p->ks_len[j], p->causal) != RA_CLASS_SKIP;
+    for (int j = 0; j < p->nks; ++j) any |= span_sees(qs.start, qs.len, p->ks_start[j], p->ks_len[j], p->causal, m);
     if (qs.len > 0 && (any || !accum)) {
       p->qs_start[p->nqs] = qs.start;
       p->qs_len[p->nqs] = qs.len;
@@ -261,9 +312,18 @@ int ra_step(const ra_step_desc* d, const void* q, const void* k, const void* v, 
 
 int ra_rank_forward(const ra_rank_desc* d, const void* q_local, const void* k_shards, const void* v_shards,
                     float* o, float* lse, void* stream) {
+  return ra_rank_forward_masked(d, nullptr, q_local, k_shards, v_shards, o, lse, stream);
+}
+
+int ra_rank_forward_masked(const ra_rank_desc* d, const ra_mask* m, const void* q_local, const void* k_shards,
+                           const void* v_shards, float* o, float* lse, void* stream) {
   if (!d) return fail(RA_E_INVAL, "descriptor is NULL");
   int rc = check_ring(d->order, d->S, d->P, d->rank);
   if (rc) return rc;
+  rc = check_mask(m, d->S, d->causal != 0);
+  if (rc) return rc;
+  if (m && (m->window > 0 || m->n_seqs > 0) && d->dtype != RA_DTYPE_BF16)
+    return fail(RA_E_UNSUPPORTED, "sliding-window and packed-sequence masks are built for bf16");
   const int64_t s_loc = d->S / d->P;
   const size_t esz = d->dtype == RA_DTYPE_BF16 ? 2 : 4;
   // Validate every step's descriptor before the first launch.
@@ -297,7 +357,7 @@ int ra_rank_forward(const ra_rank_desc* d, const void* q_local, const void* k_sh
     const char* kp = (const char*)k_shards + (size_t)src * shard_elems * esz;
     const char* vp = (const char*)v_shards + (size_t)src * shard_elems * esz;
     ra::StepParams p;
-    if (!build_params(&sd, q_local, kp, vp, o, lse, s > 0, &p)) continue;
+    if (!build_params(&sd, q_local, kp, vp, o, lse, s > 0, &p, m)) continue;
     rc = launch_step(p, d->dtype, d->D, stream);
     if (rc) return rc;
   }

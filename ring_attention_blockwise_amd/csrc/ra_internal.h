@@ -34,6 +34,10 @@ struct StepParams {
   int nqs, nks;
   long long qs_start[2], qs_len[2], qs_off[2];
   long long ks_start[2], ks_len[2], ks_off[2];
+  long long window;         // > 0: a query sees its `window` most recent keys (causal only)
+  const long long* cu;      // packed sequences: boundaries cu[0..nseg] (device), or null
+  int nseg;
+  int mask_ext;             // window or packed sequences in use
   int qt_span0;             // query tiles in listed query span 0
   int n_qtiles;             // query tiles per (batch, head)
   int n_work;               // B * Hq * n_qtiles
