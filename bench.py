@@ -212,6 +212,42 @@ def time_backward(ra, w, rank, reps=3):
             "frac_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "finite": ok}
 
 
+def masked_pairs(w, rank, window):
+    """Visible (query, key) pairs per (batch, head) of one rank under a
+    causal sliding window: query t sees min(t + 1, window) keys."""
+    spans = []
+    if w.order == "zigzag":
+        c = w.S // (2 * w.P)
+        spans = [(rank * c, c), ((2 * w.P - 1 - rank) * c, c)]
+    else:
+        c = w.S // w.P
+        spans = [(rank * c, c)]
+    t = np.concatenate([np.arange(a, a + n, dtype=np.int64) for a, n in spans])
+    return int(np.minimum(t + 1, window).sum())
+
+
+def time_window(ra, w, rank, window, reps=5):
+    """The same rank's ring with a causal sliding window: masked tiles at both
+    ends of each row's key range, hidden tiles and steps skipped."""
+    import torch
+    q, ks, vs, o, lse = build_inputs(ra, w, rank)
+    kw = dict(S=w.S, P=w.P, rank=rank, order=w.order, causal=True, scale=w.scale, window=window)
+    ra.ra_rank_forward_masked(q, ks, vs, o, lse, **kw)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        ra.ra_rank_forward_masked(q, ks, vs, o, lse, **kw)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = 4.0 * w.D * w.B * w.Hq * masked_pairs(w, rank, window)
+    del q, ks, vs, o, lse
+    torch.cuda.empty_cache()
+    return {"kernel": f"rank_forward_window{window}", "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "frac_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def time_merge(ra, rows, D, reps=20):
     """Standalone merge, rotating buffer sets so the working set exceeds the
     256 MB Infinity Cache."""
@@ -379,6 +415,8 @@ def main():
     aux = []
     if not args.no_aux:
         aux.append(time_allgather(ra, w, rank, ms))
+        if w.dtype == "bf16" and w.causal:
+            aux.append(time_window(ra, w, rank, 4096))
         if w.dtype == "bf16" and w.D == 128:
             aux.append(time_backward(ra, w, rank))
         aux.append(time_merge(ra, w.B * (w.S // w.P) * w.Hq, w.D))
