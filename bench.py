@@ -35,7 +35,7 @@ METRIC = "attention TFLOPS per rank-share (1 GPU) and % of bf16 MFMA peak"
 KERNEL_SOURCES = ["ring_attention_blockwise_amd/csrc/attn_step_bf16.hip",
                   "ring_attention_blockwise_amd/csrc/attn_common.h",
                   "ring_attention_blockwise_amd/csrc/ra_internal.h"]
-KERNEL_NAME = "attn_step_bf16_kernel<128>"
+KERNEL_NAME = "attn_step_bf16_kernel<128, false>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_step_traffic.json")
 
 
