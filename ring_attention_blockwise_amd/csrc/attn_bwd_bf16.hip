@@ -13,19 +13,22 @@
 //   dQ += scale dS K,  dK += scale dS^T Q,  dV += P^T dO,
 // with the G query heads of a group adding into their shared K/V head.
 //
-// Two kernels, so that no two workgroups add into the same rows:
+// Three kernels; in none of them do two workgroups add into the same rows:
 //   * dQ: a workgroup (4 waves) owns 128 query rows of one (batch, query
 //     head), 32 per wave, and walks the step's key tiles like the forward
 //     kernel: S^T = K Q^T and dP^T = V dO^T (K, V rows from LDS, Q^T and dO^T
 //     in registers), then dQ^T += K^T dS^T with K^T gathered by transposing
 //     LDS reads.
-//   * dK/dV: a workgroup owns 128 keys of one (batch, kv head), 32 per wave,
-//     with K^T in registers and V in LDS for the whole item, and walks the
-//     query tiles (32 rows) of every query head of the group that see them:
-//     S = Q K^T and dP = dO V^T (Q, dO rows from LDS), then dV^T += dO^T P and
-//     dK^T += Q^T dS with dO^T, Q^T by transposing LDS reads.  The softmax
-//     rows are spread over the accumulator registers here, so the rows' L and
-//     delta come from LDS as 16 values per lane.
+//   * dV and dK (two kernels of one template): a workgroup owns 128 keys of
+//     one (batch, kv head), 32 per wave, with K^T (and for dK V^T) in
+//     registers for the whole item, and walks the query tiles (32 rows) of
+//     every query head of the group that see them: S = Q K^T (Q rows from
+//     LDS), then dV^T += dO^T P; or S and dP = dO V^T, then dK^T += Q^T dS,
+//     with dO^T, Q^T by transposing LDS reads.  Fused, the two need about 290
+//     registers (one wave per SIMD); split, 172 and 228 (two per SIMD), for
+//     one more product (S twice).  The softmax rows are spread over the
+//     accumulator registers here, so the rows' L and delta come from LDS as 16
+//     values per lane.
 // Tiles are copied global -> LDS by buffer loads with the LDS bit.  One LDS
 // layout serves both read patterns: chunk c of row r sits at c ^ csw(r), with
 // csw(r) = 4 (r mod 4) + (r / 4) mod 4, which keeps the 16 rows of a row read
@@ -405,17 +408,20 @@ struct KvStage {
   }
 };
 
+// kDK = false: dV^T += dO^T P (needs S only); kDK = true: dK^T += Q^T dS
+// (needs S and dP).  Two kernels instead of one keep each within 256
+// registers, so two waves share every SIMD.
+template <bool kDK>
 struct KvState {
-  bf16x8 k[kD / 16];     // K^T operand: K[key l%32][16u + 8(l/32) .. +7]
-  f32x16 dk[kD / 32];    // dK^T accumulators
-  f32x16 dv[kD / 32];    // dV^T accumulators
+  bf16x8 k[kD / 16];               // K^T operand: K[key l%32][16u + 8(l/32) .. +7]
+  bf16x8 v[kDK ? kD / 16 : 1];     // V^T operand, same layout (dP = dO V^T)
+  f32x16 acc[kD / 32];             // dK^T or dV^T accumulators
 };
 
-template <int PAR>
-__device__ inline void kv_tile(KvState& st, const BwdParams& bp, const QPlan& qp, const KvItem& it,
+template <int PAR, bool kDK>
+__device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPlan& qp, const KvItem& it,
                                const KvStage& stg, QCursor& cur, int t, RA_LDS char* const* qbuf,
-                               RA_LDS char* const* dbuf, RA_LDS char* const* lbuf, RA_LDS char* vt,
-                               unsigned lane, int wave) {
+                               RA_LDS char* const* dbuf, RA_LDS char* const* lbuf, unsigned lane, int wave) {
   const StepParams& p = bp.s;
   const QCursor ci = cur;
   if (t + 1 < qp.n) {
@@ -431,24 +437,16 @@ __device__ inline void kv_tile(KvState& st, const BwdParams& bp, const QPlan& qp
   const bool live = has_keys && (!p.causal || kwg <= qglob + qcount - 1);
   if (live) {
     const unsigned rb = row_base_sigma(lane);
-    const unsigned vb = row_base_plain(lane) + (unsigned)(32 * wave * kRowB);
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int u = 0; u < kD / 16; ++u) {
       const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(qbuf[PAR], rb ^ (32u * u)));
-      const bf16x8 b = __builtin_bit_cast(bf16x8, lds_load16(dbuf[PAR], rb ^ (32u * u)));
-      const bf16x8 vv = __builtin_bit_cast(bf16x8, lds_load16(vt, vb ^ (32u * u)));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.k[u], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, vv, dp, 0, 0, 0);
+      if (kDK) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, lds_load16(dbuf[PAR], rb ^ (32u * u)));
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, st.v[u], dp, 0, 0, 0);
+      }
     }
-    // operand reads one unit ahead of their MFMAs (bounds the registers in flight)
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-#pragma unroll
-    for (int u = 1; u < kD / 16; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
     // rows of register r: 16(r/8) + 8L + r%8 of the tile
     const int L = (int)(lane >> 5);
@@ -462,35 +460,35 @@ __device__ inline void kv_tile(KvState& st, const BwdParams& bp, const QPlan& qp
     const RA_LDS float* lt = (const RA_LDS float*)lbuf[PAR];
     unsigned b0, b1;
     tr_bases(lane, b0, b1);
-    // one 16-row half at a time: P and dS of rows 16hf .. 16hf+15, then
-    // dV^T += dO^T P and dK^T += Q^T dS over those rows
+    // one 16-row half at a time: P (and dS) of rows 16hf .. 16hf+15, then the
+    // product over those rows
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const f32x4 l0 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L);
       const f32x4 l1 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L + 4);
-      const f32x4 t0 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L);
-      const f32x4 t1 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L + 4);
       const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-      const float tv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-      f32x8 x, y;
+      float tv[8];
+      if (kDK) {
+        const f32x4 t0 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L);
+        const f32x4 t1 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L + 4);
+        tv[0] = t0[0], tv[1] = t0[1], tv[2] = t0[2], tv[3] = t0[3];
+        tv[4] = t1[0], tv[5] = t1[1], tv[6] = t1[2], tv[7] = t1[3];
+      }
+      f32x8 x;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // rows past the tile's end and rows with no weight (L = -inf) give 0
         const bool ok = 16 * hf + 8 * L + e < qcount && lv[e] != kNegInf;
         const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e)) : 0.f;
-        x[e] = pr;
-        y[e] = pr * (dp[8 * hf + e] - tv[e]);
+        x[e] = kDK ? pr * (dp[8 * hf + e] - tv[e]) : pr;
       }
-      const bf16x8 pb = __builtin_convertvector(x, bf16x8);
-      const bf16x8 dsb = __builtin_convertvector(y, bf16x8);
+      const bf16x8 xb = __builtin_convertvector(x, bf16x8);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < kD / 32; ++db) {
         const unsigned o0 = (b0 ^ (64u * db)) + 16u * kRowB * hf, o1 = (b1 ^ (64u * db)) + 16u * kRowB * hf;
-        const bf16x8 ad = tr_read(dbuf[PAR], o0, o1);
-        const bf16x8 aq = tr_read(qbuf[PAR], o0, o1);
-        st.dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, pb, st.dv[db], 0, 0, 0);
-        st.dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsb, st.dk[db], 0, 0, 0);
+        const bf16x8 a = tr_read(kDK ? qbuf[PAR] : dbuf[PAR], o0, o1);
+        st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb, st.acc[db], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -499,8 +497,9 @@ __device__ inline void kv_tile(KvState& st, const BwdParams& bp, const QPlan& qp
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_bwd_dkdv_kernel(BwdParams bp) {
+template <bool kDK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_kv_kernel(BwdParams bp) {
   const StepParams& p = bp.s;
   __shared__ __attribute__((aligned(16))) char q0_raw[kTileB];
   __shared__ __attribute__((aligned(16))) char q1_raw[kTileB];
@@ -508,11 +507,9 @@ void attn_bwd_dkdv_kernel(BwdParams bp) {
   __shared__ __attribute__((aligned(16))) char d1_raw[kTileB];
   __shared__ __attribute__((aligned(16))) char l0_raw[512];
   __shared__ __attribute__((aligned(16))) char l1_raw[512];
-  __shared__ __attribute__((aligned(16))) char v_raw[kBwdKeys * kRowB];
   RA_LDS char* const qbuf[2] = {(RA_LDS char*)q0_raw, (RA_LDS char*)q1_raw};
   RA_LDS char* const dbuf[2] = {(RA_LDS char*)d0_raw, (RA_LDS char*)d1_raw};
   RA_LDS char* const lbuf[2] = {(RA_LDS char*)l0_raw, (RA_LDS char*)l1_raw};
-  RA_LDS char* const vt = (RA_LDS char*)v_raw;
   const unsigned lane = threadIdx.x & 63u;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -521,34 +518,23 @@ void attn_bwd_dkdv_kernel(BwdParams bp) {
   const QPlan qp = plan_q(p, it.kglob0);
   if (qp.n == 0) return;
 
-  // V of the item's keys into LDS (32 rows per wave, the tile layout), K^T
-  // operands into registers.
+  // K^T (and V^T) operands of the wave's 32 keys into registers
   const unsigned krow_bytes = (unsigned)(p.Hkv * kRowB);
   const long long khead = ((long long)it.b * p.Sk * p.Hkv + it.g) * (long long)kRowB;
-  const int my_keys = min(32, it.kcount - 32 * wave);
-  if (my_keys > 0) {
-    const char* vsrc = (const char*)p.v + khead + (it.klocal0 + 32 * wave) * (long long)krow_bytes;
-    const int nrec = (my_keys - 1) * (int)krow_bytes + kRowB;
-    const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)vsrc, (short)0, nrec, kRsrcWord3);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // slot i*64 + lane of the wave's 32-row block
-      const unsigned slot = (unsigned)i * 64u + lane;
-      const unsigned r = slot >> 4;
-      const unsigned o = r * krow_bytes + 16u * ((slot & 15u) ^ csw(r));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (RA_LDS void*)(vt + 32 * wave * kRowB + i * 1024), 16, (int)o, 0, 0,
-                                               0);
-    }
-  }
-  KvState st;
+  KvState<kDK> st;
   {
     const int key = 32 * wave + (int)(lane & 31u);
     const bool kok = key < it.kcount;
-    const uint16_t* krow = (const uint16_t*)((const char*)p.k + khead + (it.klocal0 + key) * (long long)krow_bytes);
+    const long long ro = khead + (it.klocal0 + key) * (long long)krow_bytes;
+    const uint16_t* krow = (const uint16_t*)((const char*)p.k + ro);
+    const uint16_t* vrow = (const uint16_t*)((const char*)p.v + ro);
 #pragma unroll
-    for (int u = 0; u < kD / 16; ++u) st.k[u] = kok ? *(const bf16x8*)(krow + 16 * u + 8 * (lane >> 5)) : bf16x8{};
+    for (int u = 0; u < kD / 16; ++u) {
+      st.k[u] = kok ? *(const bf16x8*)(krow + 16 * u + 8 * (lane >> 5)) : bf16x8{};
+      if (kDK) st.v[kDK ? u : 0] = kok ? *(const bf16x8*)(vrow + 16 * u + 8 * (lane >> 5)) : bf16x8{};
+    }
 #pragma unroll
-    for (int db = 0; db < kD / 32; ++db) st.dk[db] = st.dv[db] = f32x16{};
+    for (int db = 0; db < kD / 32; ++db) st.acc[db] = f32x16{};
   }
 
   KvStage stg;
@@ -561,37 +547,30 @@ void attn_bwd_dkdv_kernel(BwdParams bp) {
 
   int t = 0;
   for (; t + 1 < qp.n; t += 2) {
-    kv_tile<0>(st, bp, qp, it, stg, cur, t, qbuf, dbuf, lbuf, vt, lane, wave);
-    kv_tile<1>(st, bp, qp, it, stg, cur, t + 1, qbuf, dbuf, lbuf, vt, lane, wave);
+    kv_tile<0, kDK>(st, bp, qp, it, stg, cur, t, qbuf, dbuf, lbuf, lane, wave);
+    kv_tile<1, kDK>(st, bp, qp, it, stg, cur, t + 1, qbuf, dbuf, lbuf, lane, wave);
   }
-  if (t < qp.n) kv_tile<0>(st, bp, qp, it, stg, cur, t, qbuf, dbuf, lbuf, vt, lane, wave);
+  if (t < qp.n) kv_tile<0, kDK>(st, bp, qp, it, stg, cur, t, qbuf, dbuf, lbuf, lane, wave);
 
-  // dK = scale dS^T Q and dV = P^T dO of the wave's keys, added to the tensors
+  // dK = scale dS^T Q or dV = P^T dO of the wave's keys, added to the tensor
   const int key = 32 * wave + (int)(lane & 31u);
   if (key >= it.kcount) return;
   const long long krow = ((long long)it.b * p.Sk + it.klocal0 + key) * p.Hkv + it.g;
-  float* dkp = bp.dk + krow * kD;
-  float* dvp = bp.dv + krow * kD;
+  float* dst = (kDK ? bp.dk : bp.dv) + krow * kD;
+  const float f = kDK ? p.scale : 1.f;
   const int dsub = 4 * (int)(lane >> 5);
 #pragma unroll
   for (int db = 0; db < kD / 32; ++db)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = 32 * db + 8 * j + dsub;
-      const f32x16& a = st.dk[db];
-      const f32x16& b = st.dv[db];
-      float4 rk = *(const float4*)(dkp + c);
-      float4 rv = *(const float4*)(dvp + c);
-      rk.x += a[4 * j] * p.scale;
-      rk.y += a[4 * j + 1] * p.scale;
-      rk.z += a[4 * j + 2] * p.scale;
-      rk.w += a[4 * j + 3] * p.scale;
-      rv.x += b[4 * j];
-      rv.y += b[4 * j + 1];
-      rv.z += b[4 * j + 2];
-      rv.w += b[4 * j + 3];
-      *(float4*)(dkp + c) = rk;
-      *(float4*)(dvp + c) = rv;
+      const f32x16& a = st.acc[db];
+      float4 r = *(const float4*)(dst + c);
+      r.x += a[4 * j] * f;
+      r.y += a[4 * j + 1] * f;
+      r.z += a[4 * j + 2] * f;
+      r.w += a[4 * j + 3] * f;
+      *(float4*)(dst + c) = r;
     }
 }
 
@@ -632,7 +611,12 @@ hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s) {
   if (p.s.n_work > 0) hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(8 * p.s.per_xcd), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.n_kwork > 0) hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(8 * p.per_xcd_kv), dim3(kThreads), 0, s, p);
+  if (p.n_kwork > 0) {
+    hipLaunchKernelGGL(attn_bwd_kv_kernel<false>, dim3(8 * p.per_xcd_kv), dim3(kThreads), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_bwd_kv_kernel<true>, dim3(8 * p.per_xcd_kv), dim3(kThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 
