@@ -368,6 +368,51 @@ def cpu_baseline(w, rank, target_s=15.0):
                       f"float64 numpy, {done_s:.1f} s"}
 
 
+def cpu_aux_baselines(w, rank):
+    """The merge, relayout and backward oracles as they stand, timed on the
+    host on the shapes the GPU legs use (bounded samples; float64 numpy)."""
+    import seeded_inputs as si
+    from oracle import attention as oa
+    from oracle import attention_backward as ob
+    from oracle import index_maps as im
+    from oracle import relayout as rl
+    out = []
+    rng = np.random.default_rng(5)
+    rows = w.B * (w.S // w.P) * w.Hq // 8        # an eighth of the merge's rows
+    oa_, ob_ = rng.standard_normal((rows, w.D)), rng.standard_normal((rows, w.D))
+    la, lb = rng.standard_normal(rows), rng.standard_normal(rows)
+    t0 = time.perf_counter()
+    oa.lse_merge(oa_, la, ob_, lb)
+    dt = time.perf_counter() - t0
+    nbytes = rows * (12 * w.D + 12)
+    out.append({"kernel": "lse_merge", "kind": "oracle", "rows": rows, "GB/s": nbytes / dt / 1e9,
+                "sample": f"{rows} rows x {w.D} (float64 inputs; bytes counted as the GPU's float32 ones)"})
+    x = rng.standard_normal((2, 8192, 16, 128)).astype(np.float32).view(np.uint32).astype(np.uint16)
+    t0 = time.perf_counter()
+    rl.seq2head(x, 8)
+    dt = time.perf_counter() - t0
+    out.append({"kernel": "ulysses_relayout_seq2head", "kind": "oracle", "GB/s": 2 * x.nbytes / dt / 1e9,
+                "sample": "[2, 8192, 16, 128] 2-byte elements, P_u = 8"})
+    pos = im.rank_positions(w.S, w.P, rank, w.order)
+    sel = np.sort(rng.choice(pos.size, 4, replace=False))
+    qsel = pos[sel]
+    kmax = int(qsel.max()) + 1
+    q = si.to_f64(si.tokens(w.seed_id, si.TENSOR_Q, w.B, w.S, w.Hq, w.D, [(int(t), 1) for t in qsel], w.dtype), w.dtype)
+    do = si.to_f64(si.tokens(w.seed_id, si.TENSOR_DO, w.B, w.S, w.Hq, w.D, [(int(t), 1) for t in qsel], w.dtype),
+                   w.dtype)
+    K = si.to_f64(si.tokens(w.seed_id, si.TENSOR_K, w.B, w.S, w.Hkv, w.D, [(0, kmax)], w.dtype, scale=w.k_scale),
+                  w.dtype)
+    V = si.to_f64(si.tokens(w.seed_id, si.TENSOR_V, w.B, w.S, w.Hkv, w.D, [(0, kmax)], w.dtype), w.dtype)
+    t0 = time.perf_counter()
+    ob.attention_grads(q, K, V, do, w.causal, w.scale, qpos=qsel, kpos=np.arange(kmax))
+    dt = time.perf_counter() - t0
+    vis = (qsel + 1).sum() if w.causal else qsel.size * w.S
+    flops = 2.5 * 4.0 * w.D * w.B * w.Hq * float(vis)
+    out.append({"kernel": "rank_backward", "kind": "oracle", "TFLOP/s": flops / dt / 1e12,
+                "sample": f"{sel.size} random query rows of rank {rank} x {w.Hq} heads, all visible keys"})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -432,6 +477,7 @@ def main():
     if not args.no_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, rank)
+        cpu["aux"] = cpu_aux_baselines(w, rank)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
