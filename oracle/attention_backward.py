@@ -30,9 +30,9 @@ import numpy as np
 from . import index_maps as im
 
 
-def _row_block(qb, qpos, kk, vv, dob, kpos, causal, scale):
+def _row_block(qb, qpos, kk, vv, dob, kpos, causal, scale, window=0, cu_seqlens=None):
     """P, dS of a block of query rows of one head against keys kk, vv."""
-    vis = im.visible(qpos, kpos, causal)
+    vis = im.visible_masked(qpos, kpos, causal, window, cu_seqlens)
     s = scale * (qb @ kk.T)
     s = np.where(vis, s, -np.inf)
     m = s.max(axis=1)
@@ -49,12 +49,14 @@ def _row_block(qb, qpos, kk, vv, dob, kpos, causal, scale):
     return p, ds
 
 
-def attention_grads(Q, K, V, dO, causal: bool, scale: float, qpos=None, kpos=None):
+def attention_grads(Q, K, V, dO, causal: bool, scale: float, qpos=None, kpos=None, window: int = 0,
+                    cu_seqlens=None):
     """dQ, dK, dV of sum(dO * O) for O = attention(Q, K, V).
 
     Q, dO: [B, Nq, Hq, D]; K, V: [B, Nk, Hkv, D]; positions default to
     0..N-1.  With ``Q`` holding only some query rows (``qpos`` their global
-    positions), dK and dV are those rows' contributions.
+    positions), dK and dV are those rows' contributions.  ``window`` and
+    ``cu_seqlens`` select the mask variants of ``index_maps.visible_masked``.
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -73,7 +75,8 @@ def attention_grads(Q, K, V, dO, causal: bool, scale: float, qpos=None, kpos=Non
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            p, ds = _row_block(Q[b, :, h], qpos, K[b, :, g], V[b, :, g], dO[b, :, h], kpos, causal, scale)
+            p, ds = _row_block(Q[b, :, h], qpos, K[b, :, g], V[b, :, g], dO[b, :, h], kpos, causal, scale,
+                               window, cu_seqlens)
             dV[b, :, g] += p.T @ dO[b, :, h]
             dQ[b, :, h] = scale * (ds @ K[b, :, g])
             dK[b, :, g] += scale * (ds.T @ Q[b, :, h])

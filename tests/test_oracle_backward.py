@@ -9,11 +9,11 @@ from oracle import attention_backward as ob
 from oracle import index_maps as im
 
 
-def _loss_fn(dO, causal, scale):
+def _loss_fn(dO, causal, scale, window=0, cu=None):
     def loss(Q, K, V):
         pos_q = np.arange(Q.shape[1])
         pos_k = np.arange(K.shape[1])
-        o, _ = oa.attention_rows(Q, pos_q, K, V, pos_k, causal, scale)
+        o, _ = oa.attention_rows(Q, pos_q, K, V, pos_k, causal, scale, window=window, cu_seqlens=cu)
         return float((o * dO).sum())
     return loss
 
@@ -91,3 +91,26 @@ def test_rank_contributions_add_up_and_rows_are_independent():
     rows = np.array([3, 17, 30])
     np.testing.assert_allclose(ob.dq_rows(Q[:, rows], rows, K, V, dO[:, rows], True, 0.6), dQ[:, rows],
                                rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal,window,cu", [(True, 3, None), (True, 0, [0, 2, 6]), (False, 0, [0, 4, 6]),
+                                              (True, 2, [0, 3, 6])])
+def test_masked_gradients_match_finite_differences(causal, window, cu):
+    rng = np.random.default_rng(17 + window)
+    B, S, Hq, Hkv, D = 1, 6, 2, 1, 3
+    Q = rng.standard_normal((B, S, Hq, D))
+    K = rng.standard_normal((B, S, Hkv, D))
+    V = rng.standard_normal((B, S, Hkv, D))
+    dO = rng.standard_normal((B, S, Hq, D))
+    dQ, dK, dV = ob.attention_grads(Q, K, V, dO, causal, 0.9, window=window, cu_seqlens=cu)
+    loss = _loss_fn(dO, causal, 0.9, window, cu)
+    eps = 1e-6
+    for which, X, dX in (("Q", Q, dQ), ("K", K, dK), ("V", V, dV)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            args = {"Q": Q, "K": K, "V": V}
+            xp, xm = X.copy(), X.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            num[idx] = (loss(**{**args, which: xp}) - loss(**{**args, which: xm})) / (2 * eps)
+        assert np.abs(num - dX).max() < 1e-7, which
