@@ -234,6 +234,22 @@ int ra_rank_backward(const ra_rank_desc* d, const void* q_local,
                      float* delta, void* stream);
 
 /*
+ * ra_rank_backward_masked -- ra_rank_backward under a sliding window and/or
+ * packed sequences (the masks of ra_rank_forward_masked; lse and o must come
+ * from that call with the same mask).  A query's gradient terms run over the
+ * keys the mask lets it see, the same set as in the forward: hidden tiles are
+ * not visited, and a step whose whole block is hidden adds nothing to dK and
+ * dV.  m == NULL is ra_rank_backward.  Requirements and errors as for
+ * ra_rank_backward, plus the mask checks of ra_rank_forward_masked.
+ */
+int ra_rank_backward_masked(const ra_rank_desc* d, const ra_mask* m,
+                            const void* q_local, const void* k_shards,
+                            const void* v_shards, const float* o,
+                            const float* lse, const void* dout, float* dq,
+                            float* dk_shards, float* dv_shards, float* delta,
+                            void* stream);
+
+/*
  * ra_ulysses_relayout -- the local pack/unpack around the Ulysses all-to-all
  * ("Sequence Parallelism II: DeepSpeed Ulysses and All-to-All Attention": a
  * rank goes from all heads of its tokens to all tokens of a subset of heads).

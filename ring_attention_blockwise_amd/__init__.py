@@ -88,6 +88,8 @@ lib.ra_rank_forward_masked.argtypes = [ctypes.POINTER(ra_rank_desc), ctypes.POIN
                                        _fp, _fp, _vp]
 lib.ra_rank_backward.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp, _fp, _fp, _vp, _fp, _fp, _fp,
                                  _fp, _vp]
+lib.ra_rank_backward_masked.argtypes = [ctypes.POINTER(ra_rank_desc), ctypes.POINTER(ra_mask), _vp, _vp, _vp, _fp,
+                                        _fp, _vp, _fp, _fp, _fp, _fp, _vp]
 lib.ra_ulysses_relayout.argtypes = [_i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp]
 lib.ra_ulysses_pieces.argtypes = [_i32, _i32, _i32, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_void_p),
                                   ctypes.POINTER(ctypes.c_int64), _vp, _vp]
@@ -97,12 +99,12 @@ lib.ra_last_error.argtypes = []
 lib.ra_abi_version.restype = ctypes.c_int
 lib.ra_abi_version.argtypes = []
 for _f in ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_rank_forward_masked", "ra_allgather_forward",
-           "ra_rank_backward",
+           "ra_rank_backward", "ra_rank_backward_masked",
            "ra_ulysses_relayout", "ra_ulysses_pieces", "ra_plan"):
     getattr(lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_rank_forward_masked", "ra_allgather_forward",
-           "ra_rank_backward",
+           "ra_rank_backward", "ra_rank_backward_masked",
            "ra_ulysses_relayout", "ra_ulysses_pieces", "ra_plan",
            "ra_last_error", "ra_abi_version")
 
@@ -249,6 +251,14 @@ def ra_rank_forward_masked(q_local, k_shards, v_shards, o, lse, *, S: int, P: in
         raise ValueError("o must be [B, S/P, Hq, D] and lse [B, S/P, Hq]")
     d = ra_rank_desc(_dtype_code(q_local), B, Hq, Hkv, D, S, P, rank, ORDERS[order],
                      1 if causal else 0, float(scale if scale is not None else D ** -0.5))
+    m, _keep = _mask(torch, window, cu_seqlens, stream)
+    _check(lib.ra_rank_forward_masked(ctypes.byref(d), ctypes.byref(m), _ptr(q_local), _ptr(k_shards),
+                                      _ptr(v_shards), _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def _mask(torch, window, cu_seqlens, stream):
+    """An ra_mask and the buffers it points at (keep them alive across the
+    call)."""
     host = dev = None
     n = 0
     if cu_seqlens is not None:
@@ -256,13 +266,12 @@ def ra_rank_forward_masked(q_local, k_shards, v_shards, o, lse, *, S: int, P: in
         n = len(cu) - 1
         host = (ctypes.c_int64 * len(cu))(*cu)
         # allocated on the launch stream, so the stream-ordered allocator keeps
-        # it for the kernels enqueued below
+        # it for the kernels enqueued by the call
         with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
             dev = torch.tensor(cu, dtype=torch.int64, device="cuda")
     m = ra_mask(int(window), n, ctypes.cast(host, ctypes.POINTER(ctypes.c_int64)) if host is not None else None,
                 dev.data_ptr() if dev is not None else None)
-    _check(lib.ra_rank_forward_masked(ctypes.byref(d), ctypes.byref(m), _ptr(q_local), _ptr(k_shards),
-                                      _ptr(v_shards), _ptr(o), _ptr(lse), _stream(stream)))
+    return m, (host, dev)
 
 
 def ra_allgather_forward(q_local, k_global, v_global, o, lse, *, S: int, P: int, rank: int, order: str,
@@ -298,6 +307,29 @@ def ra_rank_backward(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, d
     lse from ra_rank_forward.  dq [B, S/P, Hq, D] float32 is written;
     dk_shards, dv_shards [P, B, S/P, Hkv, D] float32 are added to; delta
     [B, S/P, Hq] float32 is workspace (written with rowsum(dout * o))."""
+    d = _backward_desc(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_shards, delta,
+                       S=S, P=P, rank=rank, order=order, causal=causal, scale=scale)
+    _check(lib.ra_rank_backward(ctypes.byref(d), _ptr(q_local), _ptr(k_shards), _ptr(v_shards), _ptr(o),
+                                _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk_shards), _ptr(dv_shards), _ptr(delta),
+                                _stream(stream)))
+
+
+def ra_rank_backward_masked(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_shards, delta, *,
+                            S: int, P: int, rank: int, order: str, causal: bool, scale: float | None = None,
+                            window: int = 0, cu_seqlens=None, stream=None) -> None:
+    """ra_rank_backward under the masks of ra_rank_forward_masked (o, lse
+    from that call with the same ``window`` and ``cu_seqlens``)."""
+    torch = _torch()
+    d = _backward_desc(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_shards, delta,
+                       S=S, P=P, rank=rank, order=order, causal=causal, scale=scale)
+    m, _keep = _mask(torch, window, cu_seqlens, stream)
+    _check(lib.ra_rank_backward_masked(ctypes.byref(d), ctypes.byref(m), _ptr(q_local), _ptr(k_shards),
+                                       _ptr(v_shards), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk_shards),
+                                       _ptr(dv_shards), _ptr(delta), _stream(stream)))
+
+
+def _backward_desc(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_shards, delta, *,
+                   S, P, rank, order, causal, scale):
     torch = _torch()
     _require(q_local, "q_local", ndim=4)
     for t, n in ((k_shards, "k_shards"), (v_shards, "v_shards")):
@@ -317,11 +349,8 @@ def ra_rank_backward(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, d
         raise ValueError("o, dout and dq must be [B, S/P, Hq, D]")
     if tuple(lse.shape) != (B, s_loc, Hq) or tuple(delta.shape) != (B, s_loc, Hq):
         raise ValueError("lse and delta must be [B, S/P, Hq]")
-    d = ra_rank_desc(_dtype_code(q_local), B, Hq, Hkv, D, S, P, rank, ORDERS[order],
-                     1 if causal else 0, float(scale if scale is not None else D ** -0.5))
-    _check(lib.ra_rank_backward(ctypes.byref(d), _ptr(q_local), _ptr(k_shards), _ptr(v_shards), _ptr(o),
-                                _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk_shards), _ptr(dv_shards), _ptr(delta),
-                                _stream(stream)))
+    return ra_rank_desc(_dtype_code(q_local), B, Hq, Hkv, D, S, P, rank, ORDERS[order],
+                        1 if causal else 0, float(scale if scale is not None else D ** -0.5))
 
 
 def ra_lse_merge(o_a, lse_a, o_b, lse_b, o_out, lse_out, *, stream=None) -> None:

@@ -42,6 +42,7 @@ using namespace dev;
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 constexpr int kD = 128;
 constexpr int kThreads = 256;
@@ -135,10 +136,11 @@ struct DqState {
   float dlt;            // delta of the lane's row
 };
 
-template <int PAR>
+template <int PAR, bool kExt>
 __device__ inline void dq_tile(DqState& st, const BwdParams& bp, const TilePlan& tp, const WorkItem& wi,
                                const DqStage& stg, TileCursor& cur, int t, RA_LDS char* const* kbuf,
-                               RA_LDS char* const* vbuf, unsigned lane, int wave) {
+                               RA_LDS char* const* vbuf, const RA_LDS int* row_lo, const RA_LDS int* row_hi,
+                               unsigned lane, int wave) {
   const StepParams& p = bp.s;
   const TileCursor ti = cur;
   if (t + 1 < tp.n) {
@@ -161,10 +163,19 @@ __device__ inline void dq_tile(DqState& st, const BwdParams& bp, const TilePlan&
     // is below lim
     const long long d0 = wi.qglob0 - ti.glob0 + 1;
     const int dc = p.causal ? (int)max(-1024LL, min(1024LL, d0)) : 1024;
-    const int lim = min(ti.count(), max(0, dc + 32 * wave + (int)(lane & 31u)));
+    const int ri = 32 * wave + (int)(lane & 31u);
+    int lim = min(ti.count(), max(0, dc + ri));
+    // window, packed sequences: the row's key range [lo, hi] from LDS
+    const int base = kExt ? (int)max(-(1LL << 30), min(1LL << 30, ti.glob0 - wi.qglob0)) : 0;
+    if (kExt) lim = max(0, min(ti.count(), row_hi[ri] + 1 - base));
     const int lim_l = lim - 8 * L - 1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = neg_inf_select(lim_l - (16 * (r >> 3) + (r & 7)), s[r]);
+    if (kExt) {
+      const int lo_l = 8 * L - max(-1, min(33, row_lo[ri] - base));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = neg_inf_select(lo_l + (16 * (r >> 3) + (r & 7)), s[r]);
+    }
   }
   // P^T = exp2(S^T sl2 - L log2 e); dS^T = P^T (dP^T - delta), rounded to bf16
   bf16x8 dsb[2];
@@ -193,6 +204,7 @@ __device__ inline void dq_tile(DqState& st, const BwdParams& bp, const TilePlan&
   __syncthreads();
 }
 
+template <bool kExt>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(BwdParams bp) {
   const StepParams& p = bp.s;
@@ -202,6 +214,9 @@ void attn_bwd_dq_kernel(BwdParams bp) {
   __shared__ __attribute__((aligned(16))) char v1_raw[kTileB];
   RA_LDS char* const kbuf[2] = {(RA_LDS char*)k0_raw, (RA_LDS char*)k1_raw};
   RA_LDS char* const vbuf[2] = {(RA_LDS char*)v0_raw, (RA_LDS char*)v1_raw};
+  __shared__ int lo_raw[kBwdRows], hi_raw[kBwdRows];
+  const RA_LDS int* row_lo = (const RA_LDS int*)lo_raw;
+  const RA_LDS int* row_hi = (const RA_LDS int*)hi_raw;
   const unsigned lane = threadIdx.x & 63u;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -220,6 +235,16 @@ void attn_bwd_dq_kernel(BwdParams bp) {
         for (int j = 0; j < 4; ++j) *(float4*)(bp.dq + orow * kD + 32 * db + 8 * j + dsub) = float4{0.f, 0.f, 0.f, 0.f};
     }
     return;
+  }
+
+  if (kExt) {
+    // visible key range of each row of the work item, relative to its first
+    // row (read after the barrier below)
+    for (int r = threadIdx.x; r < kBwdRows; r += kThreads) {
+      const long long tq = wi.qglob0 + r;
+      lo_raw[r] = (int)max(-(1LL << 30), min(1LL << 30, key_lo(p, tq) - wi.qglob0));
+      hi_raw[r] = (int)max(-(1LL << 30), min(1LL << 30, key_hi(p, tq) - wi.qglob0));
+    }
   }
 
   DqStage stg;
@@ -248,10 +273,10 @@ void attn_bwd_dq_kernel(BwdParams bp) {
 
   int t = 0;
   for (; t + 1 < tp.n; t += 2) {
-    dq_tile<0>(st, bp, tp, wi, stg, cur, t, kbuf, vbuf, lane, wave);
-    dq_tile<1>(st, bp, tp, wi, stg, cur, t + 1, kbuf, vbuf, lane, wave);
+    dq_tile<0, kExt>(st, bp, tp, wi, stg, cur, t, kbuf, vbuf, row_lo, row_hi, lane, wave);
+    dq_tile<1, kExt>(st, bp, tp, wi, stg, cur, t + 1, kbuf, vbuf, row_lo, row_hi, lane, wave);
   }
-  if (t < tp.n) dq_tile<0>(st, bp, tp, wi, stg, cur, t, kbuf, vbuf, lane, wave);
+  if (t < tp.n) dq_tile<0, kExt>(st, bp, tp, wi, stg, cur, t, kbuf, vbuf, row_lo, row_hi, lane, wave);
 
   if (!row_ok) return;
   float* dst = bp.dq + orow * kD;
@@ -332,19 +357,31 @@ __device__ inline bool decode_kv(const BwdParams& bp, KvItem& it) {
   return true;
 }
 
-__device__ inline QPlan plan_q(const StepParams& p, long long kglob0) {
+// Rows of a query span that see some key of [k0, k1] (global positions):
+// key_hi and key_lo never decrease along the rows, so they are the rows t
+// with key_hi(t) >= k0 and key_lo(t) <= k1, one interval [t0, t1].
+__device__ inline void rows_seeing(const StepParams& p, long long k0, long long k1, long long& t0, long long& t1) {
+  t0 = p.causal ? k0 : (p.cu ? p.cu[seg_of(p, k0)] : 0);
+  t1 = 0x3fffffffffffffffLL;
+  if (p.window > 0) t1 = k1 + p.window - 1;
+  if (p.cu) t1 = min(t1, p.cu[seg_of(p, k1) + 1] - 1);
+}
+
+__device__ inline QPlan plan_q(const StepParams& p, long long kglob0, int kcount) {
   QPlan qp;
   qp.per_head = 0;
+  long long t0, t1;
+  rows_seeing(p, kglob0, kglob0 + kcount - 1, t0, t1);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     int b = 0, e = 0;
     if (s < p.nqs) {
-      long long first = 0;
-      if (p.causal) first = max(0LL, kglob0 - p.qs_start[s]);
       const long long len = p.qs_len[s];
-      if (first < len) {
+      const long long first = max(0LL, t0 - p.qs_start[s]);
+      const long long last = min(len - 1, t1 - p.qs_start[s]);
+      if (first <= last) {
         b = (int)(first / 32);
-        e = (int)((len + 31) / 32);
+        e = (int)(last / 32 + 1);
       }
     }
     qp.tbeg[s] = b;
@@ -379,6 +416,7 @@ struct KvStage {
   }
   // Query tile `c` of head h: 32 rows of Q and dO, and L, delta of the rows
   // (lanes 0..63 of one 4-byte copy each; rows past the tile's end read 0).
+  template <bool kExt>
   __device__ void issue(const StepParams& p, const QPlan& qp, const QCursor& c, int g, unsigned lane,
                         RA_LDS char* qdst, RA_LDS char* ddst, RA_LDS char* ldst) const {
     (void)qp;
@@ -404,6 +442,12 @@ struct KvStage {
       const auto rl = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nr, kRsrcWord3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (RA_LDS void*)(ldst + wave * 256), 4, (int)(lane * (unsigned)Hq * 4u),
                                                0, 0, 0);
+    } else if (kExt && lane < 32) {
+      // masks: key range [lo, hi] of each row, relative to the tile's first
+      // row (wave 2: lo, wave 3: hi), at ldst[512, 768)
+      const long long qg = (c.span ? p.qs_start[1] : p.qs_start[0]) + (long long)c.tile * 32;
+      const long long v = wave == 2 ? key_lo(p, qg + lane) : key_hi(p, qg + lane);
+      ((RA_LDS int*)(ldst + 512))[(wave - 2) * 32 + lane] = (int)max(-(1LL << 30), min(1LL << 30, v - qg));
     }
   }
 };
@@ -418,7 +462,7 @@ struct KvState {
   f32x16 acc[kD / 32];             // dK^T or dV^T accumulators
 };
 
-template <int PAR, bool kDK>
+template <int PAR, bool kDK, bool kExt>
 __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPlan& qp, const KvItem& it,
                                const KvStage& stg, QCursor& cur, int t, RA_LDS char* const* qbuf,
                                RA_LDS char* const* dbuf, RA_LDS char* const* lbuf, unsigned lane, int wave) {
@@ -426,7 +470,7 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
   const QCursor ci = cur;
   if (t + 1 < qp.n) {
     cur.advance(qp);
-    stg.issue(p, qp, cur, it.g, lane, qbuf[PAR ^ 1], dbuf[PAR ^ 1], lbuf[PAR ^ 1]);
+    stg.template issue<kExt>(p, qp, cur, it.g, lane, qbuf[PAR ^ 1], dbuf[PAR ^ 1], lbuf[PAR ^ 1]);
   }
   // this wave's keys against the tile's rows
   const long long qin = (long long)ci.tile * 32;
@@ -451,7 +495,11 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
     // rows of register r: 16(r/8) + 8L + r%8 of the tile
     const int L = (int)(lane >> 5);
     const int key = (int)(lane & 31u);
-    if (p.causal && kwg + 31 > qglob) {
+    // window, packed sequences: row i sees key j iff lo_i <= j <= hi_i, the
+    // row's range relative to the tile's first row (staged with the tile)
+    const RA_LDS int* rt = (const RA_LDS int*)(lbuf[PAR] + 512);
+    const int dk = kExt ? (int)max(-(1LL << 30), min(1LL << 30, kwg - qglob)) + key : 0;
+    if (!kExt && p.causal && kwg + 31 > qglob) {
       // row i sees key j iff qglob + i >= kwg + j
       const int dd = (int)max(-1024LL, min(1024LL, qglob - kwg)) + 8 * L - key;
 #pragma unroll
@@ -474,11 +522,21 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
         tv[0] = t0[0], tv[1] = t0[1], tv[2] = t0[2], tv[3] = t0[3];
         tv[4] = t1[0], tv[5] = t1[1], tv[6] = t1[2], tv[7] = t1[3];
       }
+      int lo[8], hi[8];
+      if (kExt) {
+        const i32x4 a0 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L);
+        const i32x4 a1 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L + 4);
+        const i32x4 c0 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L);
+        const i32x4 c1 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lo[e] = a0[e], lo[e + 4] = a1[e], hi[e] = c0[e], hi[e + 4] = c1[e];
+      }
       f32x8 x;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        // rows past the tile's end and rows with no weight (L = -inf) give 0
-        const bool ok = 16 * hf + 8 * L + e < qcount && lv[e] != kNegInf;
+        // rows past the tile's end, rows with no weight (L = -inf) and, under
+        // masks, keys outside the row's range give 0
+        const bool ok = 16 * hf + 8 * L + e < qcount && lv[e] != kNegInf && (!kExt || (lo[e] <= dk && dk <= hi[e]));
         const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e)) : 0.f;
         x[e] = kDK ? pr * (dp[8 * hf + e] - tv[e]) : pr;
       }
@@ -497,7 +555,7 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
   __syncthreads();
 }
 
-template <bool kDK>
+template <bool kDK, bool kExt>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_kv_kernel(BwdParams bp) {
   const StepParams& p = bp.s;
@@ -505,8 +563,8 @@ void attn_bwd_kv_kernel(BwdParams bp) {
   __shared__ __attribute__((aligned(16))) char q1_raw[kTileB];
   __shared__ __attribute__((aligned(16))) char d0_raw[kTileB];
   __shared__ __attribute__((aligned(16))) char d1_raw[kTileB];
-  __shared__ __attribute__((aligned(16))) char l0_raw[512];
-  __shared__ __attribute__((aligned(16))) char l1_raw[512];
+  __shared__ __attribute__((aligned(16))) char l0_raw[768];  // L, delta, and with masks the rows' key ranges
+  __shared__ __attribute__((aligned(16))) char l1_raw[768];
   RA_LDS char* const qbuf[2] = {(RA_LDS char*)q0_raw, (RA_LDS char*)q1_raw};
   RA_LDS char* const dbuf[2] = {(RA_LDS char*)d0_raw, (RA_LDS char*)d1_raw};
   RA_LDS char* const lbuf[2] = {(RA_LDS char*)l0_raw, (RA_LDS char*)l1_raw};
@@ -515,7 +573,7 @@ void attn_bwd_kv_kernel(BwdParams bp) {
 
   KvItem it;
   if (!decode_kv(bp, it)) return;
-  const QPlan qp = plan_q(p, it.kglob0);
+  const QPlan qp = plan_q(p, it.kglob0, it.kcount);
   if (qp.n == 0) return;
 
   // K^T (and V^T) operands of the wave's 32 keys into registers
@@ -541,16 +599,16 @@ void attn_bwd_kv_kernel(BwdParams bp) {
   stg.init(bp, it, wave, lane);
   QCursor cur;
   cur.first(qp);
-  stg.issue(p, qp, cur, it.g, lane, qbuf[0], dbuf[0], lbuf[0]);
+  stg.template issue<kExt>(p, qp, cur, it.g, lane, qbuf[0], dbuf[0], lbuf[0]);
   wait_loads();
   __syncthreads();
 
   int t = 0;
   for (; t + 1 < qp.n; t += 2) {
-    kv_tile<0, kDK>(st, bp, qp, it, stg, cur, t, qbuf, dbuf, lbuf, lane, wave);
-    kv_tile<1, kDK>(st, bp, qp, it, stg, cur, t + 1, qbuf, dbuf, lbuf, lane, wave);
+    kv_tile<0, kDK, kExt>(st, bp, qp, it, stg, cur, t, qbuf, dbuf, lbuf, lane, wave);
+    kv_tile<1, kDK, kExt>(st, bp, qp, it, stg, cur, t + 1, qbuf, dbuf, lbuf, lane, wave);
   }
-  if (t < qp.n) kv_tile<0, kDK>(st, bp, qp, it, stg, cur, t, qbuf, dbuf, lbuf, lane, wave);
+  if (t < qp.n) kv_tile<0, kDK, kExt>(st, bp, qp, it, stg, cur, t, qbuf, dbuf, lbuf, lane, wave);
 
   // dK = scale dS^T Q or dV = P^T dO of the wave's keys, added to the tensor
   const int key = 32 * wave + (int)(lane & 31u);
@@ -608,14 +666,28 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(long long rows, const T*
 }  // namespace
 
 hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s) {
-  if (p.s.n_work > 0) hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(8 * p.s.per_xcd), dim3(kThreads), 0, s, p);
+  const bool ext = p.s.mask_ext != 0;
+  if (p.s.n_work > 0) {
+    if (ext)
+      hipLaunchKernelGGL(attn_bwd_dq_kernel<true>, dim3(8 * p.s.per_xcd), dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(attn_bwd_dq_kernel<false>, dim3(8 * p.s.per_xcd), dim3(kThreads), 0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.n_kwork > 0) {
-    hipLaunchKernelGGL(attn_bwd_kv_kernel<false>, dim3(8 * p.per_xcd_kv), dim3(kThreads), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_bwd_kv_kernel<true>, dim3(8 * p.per_xcd_kv), dim3(kThreads), 0, s, p);
+    const dim3 grid(8 * p.per_xcd_kv);
+    if (ext) {
+      hipLaunchKernelGGL((attn_bwd_kv_kernel<false, true>), grid, dim3(kThreads), 0, s, p);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_bwd_kv_kernel<true, true>), grid, dim3(kThreads), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_kv_kernel<false, false>), grid, dim3(kThreads), 0, s, p);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_bwd_kv_kernel<true, false>), grid, dim3(kThreads), 0, s, p);
+    }
   }
   return hipGetLastError();
 }

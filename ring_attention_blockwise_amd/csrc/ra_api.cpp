@@ -397,11 +397,20 @@ int ra_allgather_forward(const ra_rank_desc* d, const void* q_local, const void*
 int ra_rank_backward(const ra_rank_desc* d, const void* q_local, const void* k_shards, const void* v_shards,
                      const float* o, const float* lse, const void* dout, float* dq, float* dk_shards,
                      float* dv_shards, float* delta, void* stream) {
+  return ra_rank_backward_masked(d, nullptr, q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_shards,
+                                 delta, stream);
+}
+
+int ra_rank_backward_masked(const ra_rank_desc* d, const ra_mask* m, const void* q_local, const void* k_shards,
+                            const void* v_shards, const float* o, const float* lse, const void* dout, float* dq,
+                            float* dk_shards, float* dv_shards, float* delta, void* stream) {
   if (!d) return fail(RA_E_INVAL, "descriptor is NULL");
   int rc = check_ring(d->order, d->S, d->P, d->rank);
   if (rc) return rc;
   if (d->dtype != RA_DTYPE_BF16 || d->D != 128)
     return fail(RA_E_UNSUPPORTED, "the backward pass is built for bf16 with D = 128");
+  rc = check_mask(m, d->S, d->causal != 0);
+  if (rc) return rc;
   const int64_t s_loc = d->S / d->P;
   ra_step_desc sd;
   sd.dtype = d->dtype;
@@ -437,7 +446,7 @@ int ra_rank_backward(const ra_rank_desc* d, const void* q_local, const void* k_s
     const char* kp = (const char*)k_shards + (size_t)src * shard_elems * 2;
     const char* vp = (const char*)v_shards + (size_t)src * shard_elems * 2;
     ra::BwdParams bp;
-    if (!build_params(&sd, q_local, kp, vp, nullptr, nullptr, s > 0, &bp.s)) continue;
+    if (!build_params(&sd, q_local, kp, vp, nullptr, nullptr, s > 0, &bp.s, m)) continue;
     // the dQ kernel's query tiles are kBwdRows rows
     bp.s.qt_span0 = (int)((bp.s.qs_len[0] + ra::kBwdRows - 1) / ra::kBwdRows);
     bp.s.n_qtiles = bp.s.qt_span0 + (int)((bp.s.qs_len[1] + ra::kBwdRows - 1) / ra::kBwdRows);
