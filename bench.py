@@ -175,10 +175,11 @@ def time_allgather(ra, w, rank, ring_ms, reps=5):
             "ring_over_allgather": ring_ms / ms}
 
 
-def time_backward(ra, w, rank, reps=3):
+def time_backward(ra, w, rank, reps=3, window=0):
     """The backward pass of the same rank (reverse ring, dQ and dK/dV
-    kernels per step), after one forward.  Algorithmic work: 2.5 times the
-    forward's (five products per visible pair instead of two)."""
+    kernels per step), after one forward; with ``window`` > 0 both under a
+    causal sliding window.  Algorithmic work: 2.5 times the forward's (five
+    products per visible pair instead of two)."""
     import torch
     import seeded_inputs as si
     q, ks, vs, o, lse = build_inputs(ra, w, rank)
@@ -190,10 +191,17 @@ def time_backward(ra, w, rank, reps=3):
     dv = torch.zeros_like(dk)
     delta = torch.empty((w.B, s_loc, w.Hq), dtype=torch.float32, device="cuda")
     kw = dict(S=w.S, P=w.P, rank=rank, order=w.order, causal=w.causal, scale=w.scale)
-    ra.ra_rank_forward(q, ks, vs, o, lse, **kw)
+    if window:
+        kw["window"] = window
+        ra.ra_rank_forward_masked(q, ks, vs, o, lse, **kw)
+    else:
+        ra.ra_rank_forward(q, ks, vs, o, lse, **kw)
 
     def run():
-        ra.ra_rank_backward(q, ks, vs, o, lse, do, dq, dk, dv, delta, **kw)
+        if window:
+            ra.ra_rank_backward_masked(q, ks, vs, o, lse, do, dq, dk, dv, delta, **kw)
+        else:
+            ra.ra_rank_backward(q, ks, vs, o, lse, do, dq, dk, dv, delta, **kw)
 
     run()
     torch.cuda.synchronize()
@@ -204,11 +212,11 @@ def time_backward(ra, w, rank, reps=3):
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
-    flops = 2.5 * algorithmic_flops(w, rank)
+    flops = 2.5 * (4.0 * w.D * w.B * w.Hq * masked_pairs(w, rank, window) if window else algorithmic_flops(w, rank))
     ok = bool(torch.isfinite(dq).all().item() and torch.isfinite(dk).all().item())
     del q, ks, vs, o, lse, do, dq, dk, dv, delta
     torch.cuda.empty_cache()
-    return {"kernel": "rank_backward", "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+    return {"kernel": f"rank_backward_window{window}" if window else "rank_backward", "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
             "frac_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "finite": ok}
 
 
@@ -464,6 +472,7 @@ def main():
             aux.append(time_window(ra, w, rank, 4096))
         if w.dtype == "bf16" and w.D == 128:
             aux.append(time_backward(ra, w, rank))
+            aux.append(time_backward(ra, w, rank, window=4096))
         aux.append(time_merge(ra, w.B * (w.S // w.P) * w.Hq, w.D))
         aux.append(time_relayout(ra, 2, 8192, 16, 128, 8))
         aux.extend(time_ulysses_pieces(ra, 2, 8192, 16, 128, 8))

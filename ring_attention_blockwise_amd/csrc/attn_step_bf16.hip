@@ -231,29 +231,17 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
       int lim = min(ti.count(), max(0, dc + ri));
       if (kExt) lim = max(0, min(ti.count(), row_hi[ri] + 1 - base));
       // key of register r is 16(r/8) + r%8 + 8L: it is visible iff
-      // lim - 8L - 1 - (16(r/8) + r%8) >= 0
+      // lim - 8L - 1 - (16(r/8) + r%8) >= 0 and, with a lower end lo,
+      // 16(r/8) + r%8 + 8L - lo >= 0; one sign test of the two ORed
       const int lim_l = lim - 8 * L - 1;
+      const int lo_l = kExt ? 8 * L - max(-1, min(33, row_lo[ri] - base)) : 0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         int d = lim_l - (16 * (r >> 3) + (r & 7));
+        if (kExt) d |= lo_l + (16 * (r >> 3) + (r & 7));
         asm volatile("" : "+v"(d));
         const unsigned m = (unsigned)(d >> 31);
         s[qb][r] = __uint_as_float((m & 0xff800000u) | (~m & __float_as_uint(s[qb][r])));
-      }
-    }
-    if (kExt) {
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        const int ri = 64 * wave + 32 * qb + (lane & 31);
-        // visible iff key - lo >= 0
-        const int lo_l = 8 * L - max(-1, min(33, row_lo[ri] - base));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int d = lo_l + (16 * (r >> 3) + (r & 7));
-          asm volatile("" : "+v"(d));
-          const unsigned m = (unsigned)(d >> 31);
-          s[qb][r] = __uint_as_float((m & 0xff800000u) | (~m & __float_as_uint(s[qb][r])));
-        }
       }
     }
   }
