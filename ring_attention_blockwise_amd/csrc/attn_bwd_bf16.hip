@@ -534,10 +534,14 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
       f32x8 x;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        // rows past the tile's end, rows with no weight (L = -inf) and, under
-        // masks, keys outside the row's range give 0
-        const bool ok = 16 * hf + 8 * L + e < qcount && lv[e] != kNegInf && (!kExt || (lo[e] <= dk && dk <= hi[e]));
-        const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e)) : 0.f;
+        // No guard for rows past the tile's end: their Q, dO, L and delta
+        // were staged as zeros, so P = 1 there multiplies zero rows (and dS =
+        // 0).  L is finite on every real row (each row sees at least its own
+        // key), so P needs no -inf case; under masks a key outside the row's
+        // range gets exponent -inf.  A select, not a branch, before exp2.
+        float a = __builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e);
+        if (kExt) a = (lo[e] <= dk && dk <= hi[e]) ? a : kNegInf;
+        const float pr = __builtin_amdgcn_exp2f(a);
         x[e] = kDK ? pr * (dp[8 * hf + e] - tv[e]) : pr;
       }
       const bf16x8 xb = __builtin_convertvector(x, bf16x8);
