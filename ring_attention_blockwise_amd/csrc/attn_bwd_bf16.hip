@@ -319,6 +319,14 @@ struct QCursor {
     span = qp.tend[0] > qp.tbeg[0] ? 0 : 1;
     tile = span ? qp.tbeg[1] : qp.tbeg[0];
   }
+  // tile `idx` of the list (heads outer, then spans, then tiles)
+  __device__ void seek(const QPlan& qp, int idx) {
+    hh = idx / qp.per_head;
+    const int r = idx - hh * qp.per_head;
+    const int n0 = qp.tend[0] - qp.tbeg[0];
+    span = r < n0 ? 0 : 1;
+    tile = span ? qp.tbeg[1] + (r - n0) : qp.tbeg[0] + r;
+  }
   __device__ void advance(const QPlan& qp) {
     ++tile;
     const int end = span ? qp.tend[1] : qp.tend[0];
@@ -462,13 +470,16 @@ struct KvState {
   f32x16 acc[kD / 32];             // dK^T or dV^T accumulators
 };
 
+// Tile t of the list from buffer PAR while tile t+1 is copied into PAR ^ 1;
+// te: end of this wave group's part of the list (tiles at or past it only
+// keep the group in step with the other at the barrier).
 template <int PAR, bool kDK, bool kExt>
 __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPlan& qp, const KvItem& it,
-                               const KvStage& stg, QCursor& cur, int t, RA_LDS char* const* qbuf,
+                               const KvStage& stg, QCursor& cur, int t, int te, RA_LDS char* const* qbuf,
                                RA_LDS char* const* dbuf, RA_LDS char* const* lbuf, unsigned lane, int wave) {
   const StepParams& p = bp.s;
   const QCursor ci = cur;
-  if (t + 1 < qp.n) {
+  if (t + 1 < te) {
     cur.advance(qp);
     stg.template issue<kExt>(p, qp, cur, it.g, lane, qbuf[PAR ^ 1], dbuf[PAR ^ 1], lbuf[PAR ^ 1]);
   }
@@ -477,7 +488,7 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
   const long long qglob = (ci.span ? p.qs_start[1] : p.qs_start[0]) + qin;
   const int qcount = (int)min(32LL, (ci.span ? p.qs_len[1] : p.qs_len[0]) - qin);
   const long long kwg = it.kglob0 + 32 * wave;
-  const bool has_keys = 32 * wave < it.kcount;
+  const bool has_keys = 32 * wave < it.kcount && t < te;
   const bool live = has_keys && (!p.causal || kwg <= qglob + qcount - 1);
   if (live) {
     const unsigned rb = row_base_sigma(lane);
@@ -559,21 +570,58 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
   __syncthreads();
 }
 
+// One key tile's pass over its query tiles by one group of four waves (GRP),
+// tiles [tb, te) of the list; returns the accumulators in st.
 template <bool kDK, bool kExt>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__device__ __attribute__((always_inline)) inline void kv_pass(KvState<kDK>& st, const BwdParams& bp, const QPlan& qp, const KvItem& it, int tb,
+                               int te, int iters, RA_LDS char* const* qbuf, RA_LDS char* const* dbuf,
+                               RA_LDS char* const* lbuf, unsigned lane, int wave) {
+  const StepParams& p = bp.s;
+  KvStage stg;
+  stg.init(bp, it, wave, lane);
+  QCursor cur;
+  cur.first(qp);
+  if (tb > 0) cur.seek(qp, tb);
+  if (tb < te) stg.template issue<kExt>(p, qp, cur, it.g, lane, qbuf[0], dbuf[0], lbuf[0]);
+  wait_loads();
+  __syncthreads();
+
+  int i = 0;
+  for (; i + 1 < iters; i += 2) {
+    kv_tile<0, kDK, kExt>(st, bp, qp, it, stg, cur, tb + i, te, qbuf, dbuf, lbuf, lane, wave);
+    kv_tile<1, kDK, kExt>(st, bp, qp, it, stg, cur, tb + i + 1, te, qbuf, dbuf, lbuf, lane, wave);
+  }
+  if (i < iters) kv_tile<0, kDK, kExt>(st, bp, qp, it, stg, cur, tb + i, te, qbuf, dbuf, lbuf, lane, wave);
+}
+
+// kSplit = false: four waves (one workgroup) per key tile of 128 keys.
+// kSplit = true: eight waves, two groups of four over the same 128 keys; group
+// 0 takes the first half of the query-tile list and group 1 the rest, and
+// group 1 hands its partial sums to group 0 through LDS at the end (a fixed
+// order of additions, so results do not depend on timing).  For launches
+// with few key tiles: one workgroup per CU still keeps two waves on every
+// SIMD.
+template <bool kDK, bool kExt, bool kSplit>
+__global__ __launch_bounds__(kSplit ? 2 * kThreads : kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_kv_kernel(BwdParams bp) {
   const StepParams& p = bp.s;
+  constexpr int kB2 = kSplit ? kTileB : 16;  // group 1's buffers
   __shared__ __attribute__((aligned(16))) char q0_raw[kTileB];
   __shared__ __attribute__((aligned(16))) char q1_raw[kTileB];
   __shared__ __attribute__((aligned(16))) char d0_raw[kTileB];
   __shared__ __attribute__((aligned(16))) char d1_raw[kTileB];
   __shared__ __attribute__((aligned(16))) char l0_raw[768];  // L, delta, and with masks the rows' key ranges
   __shared__ __attribute__((aligned(16))) char l1_raw[768];
-  RA_LDS char* const qbuf[2] = {(RA_LDS char*)q0_raw, (RA_LDS char*)q1_raw};
-  RA_LDS char* const dbuf[2] = {(RA_LDS char*)d0_raw, (RA_LDS char*)d1_raw};
-  RA_LDS char* const lbuf[2] = {(RA_LDS char*)l0_raw, (RA_LDS char*)l1_raw};
+  __shared__ __attribute__((aligned(16))) char q2_raw[kB2];
+  __shared__ __attribute__((aligned(16))) char q3_raw[kB2];
+  __shared__ __attribute__((aligned(16))) char d2_raw[kB2];
+  __shared__ __attribute__((aligned(16))) char d3_raw[kB2];
+  __shared__ __attribute__((aligned(16))) char l2_raw[kSplit ? 768 : 16];
+  __shared__ __attribute__((aligned(16))) char l3_raw[kSplit ? 768 : 16];
   const unsigned lane = threadIdx.x & 63u;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = kSplit ? wv >> 2 : 0;
+  const int wave = wv & 3;  // the wave's 32 keys within the tile
 
   KvItem it;
   if (!decode_kv(bp, it)) return;
@@ -599,20 +647,53 @@ void attn_bwd_kv_kernel(BwdParams bp) {
     for (int db = 0; db < kD / 32; ++db) st.acc[db] = f32x16{};
   }
 
-  KvStage stg;
-  stg.init(bp, it, wave, lane);
-  QCursor cur;
-  cur.first(qp);
-  stg.template issue<kExt>(p, qp, cur, it.g, lane, qbuf[0], dbuf[0], lbuf[0]);
-  wait_loads();
-  __syncthreads();
-
-  int t = 0;
-  for (; t + 1 < qp.n; t += 2) {
-    kv_tile<0, kDK, kExt>(st, bp, qp, it, stg, cur, t, qbuf, dbuf, lbuf, lane, wave);
-    kv_tile<1, kDK, kExt>(st, bp, qp, it, stg, cur, t + 1, qbuf, dbuf, lbuf, lane, wave);
+  const int half = kSplit ? (qp.n + 1) / 2 : qp.n;
+  if (grp == 0) {
+    RA_LDS char* const qbuf[2] = {(RA_LDS char*)q0_raw, (RA_LDS char*)q1_raw};
+    RA_LDS char* const dbuf[2] = {(RA_LDS char*)d0_raw, (RA_LDS char*)d1_raw};
+    RA_LDS char* const lbuf[2] = {(RA_LDS char*)l0_raw, (RA_LDS char*)l1_raw};
+    kv_pass<kDK, kExt>(st, bp, qp, it, 0, half, half, qbuf, dbuf, lbuf, lane, wave);
+  } else {
+    RA_LDS char* const qbuf[2] = {(RA_LDS char*)q2_raw, (RA_LDS char*)q3_raw};
+    RA_LDS char* const dbuf[2] = {(RA_LDS char*)d2_raw, (RA_LDS char*)d3_raw};
+    RA_LDS char* const lbuf[2] = {(RA_LDS char*)l2_raw, (RA_LDS char*)l3_raw};
+    kv_pass<kDK, kExt>(st, bp, qp, it, half, qp.n, half, qbuf, dbuf, lbuf, lane, wave);
   }
-  if (t < qp.n) kv_tile<0, kDK, kExt>(st, bp, qp, it, stg, cur, t, qbuf, dbuf, lbuf, lane, wave);
+
+  if (kSplit) {
+    // group 1's sums into LDS (8 KB of each of two buffers per wave, the
+    // staging buffers being idle after the last barrier), then group 0 adds
+    // them; layout [4 registers][64 lanes] of float4, conflict-free
+    // (selects, not a table indexed by the wave: LDS addresses cannot be
+    // stored as data)
+    RA_LDS f32x4* const x0 = (RA_LDS f32x4*)(wave == 0   ? (RA_LDS char*)q0_raw
+                                              : wave == 1 ? (RA_LDS char*)q1_raw
+                                              : wave == 2 ? (RA_LDS char*)d0_raw
+                                                          : (RA_LDS char*)d1_raw);
+    RA_LDS f32x4* const x1 = (RA_LDS f32x4*)(wave == 0   ? (RA_LDS char*)q2_raw
+                                              : wave == 1 ? (RA_LDS char*)q3_raw
+                                              : wave == 2 ? (RA_LDS char*)d2_raw
+                                                          : (RA_LDS char*)d3_raw);
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v = {st.acc[db][4 * j], st.acc[db][4 * j + 1], st.acc[db][4 * j + 2], st.acc[db][4 * j + 3]};
+          (db < 2 ? x0 : x1)[((db & 1) * 4 + j) * 64 + lane] = v;
+        }
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = (db < 2 ? x0 : x1)[((db & 1) * 4 + j) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.acc[db][4 * j + e] += v[e];
+      }
+  }
 
   // dK = scale dS^T Q or dV = P^T dO of the wave's keys, added to the tensor
   const int key = 32 * wave + (int)(lane & 31u);
@@ -681,16 +762,20 @@ hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (p.n_kwork > 0) {
     const dim3 grid(8 * p.per_xcd_kv);
-    if (ext) {
-      hipLaunchKernelGGL((attn_bwd_kv_kernel<false, true>), grid, dim3(kThreads), 0, s, p);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((attn_bwd_kv_kernel<true, true>), grid, dim3(kThreads), 0, s, p);
+    const dim3 blk(p.kv_split ? 2 * kThreads : kThreads);
+    // dV kernel, then dK kernel
+    if (ext && p.kv_split) {
+      hipLaunchKernelGGL((attn_bwd_kv_kernel<false, true, true>), grid, blk, 0, s, p);
+      hipLaunchKernelGGL((attn_bwd_kv_kernel<true, true, true>), grid, blk, 0, s, p);
+    } else if (ext) {
+      hipLaunchKernelGGL((attn_bwd_kv_kernel<false, true, false>), grid, blk, 0, s, p);
+      hipLaunchKernelGGL((attn_bwd_kv_kernel<true, true, false>), grid, blk, 0, s, p);
+    } else if (p.kv_split) {
+      hipLaunchKernelGGL((attn_bwd_kv_kernel<false, false, true>), grid, blk, 0, s, p);
+      hipLaunchKernelGGL((attn_bwd_kv_kernel<true, false, true>), grid, blk, 0, s, p);
     } else {
-      hipLaunchKernelGGL((attn_bwd_kv_kernel<false, false>), grid, dim3(kThreads), 0, s, p);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((attn_bwd_kv_kernel<true, false>), grid, dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((attn_bwd_kv_kernel<false, false, false>), grid, blk, 0, s, p);
+      hipLaunchKernelGGL((attn_bwd_kv_kernel<true, false, false>), grid, blk, 0, s, p);
     }
   }
   return hipGetLastError();

@@ -109,6 +109,42 @@ bool span_sees(int64_t q0, int64_t nq, int64_t k0, int64_t nk, bool causal, cons
   return lo <= hi;
 }
 
+// Work of the dK/dV kernel's items: for each key tile of kBwdKeys keys, the
+// 32-row query tiles (per query head) of the rows that see some of its keys.
+// A tile [k0, k1] is seen by the rows t with key_hi(t) >= k0 and
+// key_lo(t) <= k1, one interval since both ends never decrease; the same
+// count as the kernel's own plan.  Returns the tiles with work, and the sum
+// and maximum of their query tiles.
+struct KvLoad {
+  int64_t active = 0, total = 0, max = 0;
+};
+KvLoad kv_load(const ra::StepParams& p, const ra_mask* m) {
+  const bool cu = m && m->n_seqs > 0;
+  KvLoad l;
+  for (int s = 0; s < p.nks; ++s) {
+    const int64_t end = p.ks_start[s] + p.ks_len[s];
+    for (int64_t k0 = p.ks_start[s]; k0 < end; k0 += ra::kBwdKeys) {
+      const int64_t k1 = std::min(k0 + ra::kBwdKeys, end) - 1;
+      const int64_t t0 = p.causal ? k0 : (cu ? m->cu_seqlens[seq_index(m, k0)] : 0);
+      int64_t t1 = INT64_MAX;
+      if (m && m->window > 0) t1 = k1 + m->window - 1;
+      if (cu) t1 = std::min(t1, m->cu_seqlens[seq_index(m, k1) + 1] - 1);
+      int64_t tiles = 0;
+      for (int q = 0; q < p.nqs; ++q) {
+        const int64_t first = std::max((int64_t)0, t0 - (int64_t)p.qs_start[q]);
+        const int64_t last = std::min((int64_t)p.qs_len[q] - 1, t1 - (int64_t)p.qs_start[q]);
+        if (first <= last) tiles += last / 32 - first / 32 + 1;
+      }
+      if (tiles > 0) {
+        ++l.active;
+        l.total += tiles;
+        l.max = std::max(l.max, tiles);
+      }
+    }
+  }
+  return l;
+}
+
 int check_mask(const ra_mask* m, int64_t S, bool causal) {
   if (!m) return RA_OK;
   if (m->window < 0) return fail(RA_E_INVAL, "window must be >= 0");
@@ -434,6 +470,10 @@ int ra_rank_backward_masked(const ra_rank_desc* d, const ra_mask* m, const void*
   if (!aligned(o, 16) || !aligned(dout, 16) || !aligned(dk_shards, 16) || !aligned(dv_shards, 16) ||
       !aligned(delta, 4))
     return fail(RA_E_INVAL, "o, dout, dk_shards and dv_shards must be 16-byte aligned, delta 4-byte aligned");
+  int dev = 0, n_cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return fail(RA_E_HIP, "cannot query the device's compute units");
   const int64_t rows = (int64_t)d->B * s_loc * d->Hq;
   hipError_t e = ra::launch_bwd_delta(rows, d->D, 1, dout, o, delta, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RA_E_HIP, "delta launch failed: %s", hipGetErrorString(e));
@@ -463,6 +503,13 @@ int ra_rank_backward_masked(const ra_rank_desc* d, const ra_mask* m, const void*
     bp.n_ktiles = bp.kt_span0 + (int)((bp.s.ks_len[1] + ra::kBwdKeys - 1) / ra::kBwdKeys);
     bp.n_kwork = bp.s.B * bp.s.Hkv * bp.n_ktiles;
     bp.per_xcd_kv = (bp.n_kwork + 7) / 8;
+    // Two groups of waves share each key tile's query rows (eight-wave
+    // workgroups) when the tiles with work would not give every CU a
+    // workgroup, or when the heaviest tile has half again the average work
+    // (causal and windowed diagonals): a launch lasts as long as its
+    // heaviest workgroup.
+    const KvLoad kl = kv_load(bp.s, m);
+    bp.kv_split = ((int64_t)bp.s.B * bp.s.Hkv * kl.active <= n_cus || 2 * kl.max * kl.active >= 3 * kl.total) ? 1 : 0;
     e = ra::launch_attn_bwd_bf16(bp, (hipStream_t)stream);
     if (e != hipSuccess) return fail(RA_E_HIP, "backward launch failed: %s", hipGetErrorString(e));
   }

@@ -70,6 +70,7 @@ struct BwdParams {
   int n_ktiles;          // key tiles per (batch, kv head)
   int n_kwork;           // B * Hkv * n_ktiles
   int per_xcd_kv;        // ceil(n_kwork / 8)
+  int kv_split;          // 1: two groups of four waves per key tile (few key tiles with work)
 };
 
 hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s);
