@@ -254,7 +254,18 @@ struct WorkItem {
 
 template <int BQ>
 __device__ inline bool decode_work(const StepParams& p, WorkItem& wi) {
-  const int w = (blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
+  // Workgroup i runs on XCD i mod 8; XCD x takes items [x per_xcd,
+  // (x+1) per_xcd) of the list (heads outer, query tiles last first), so
+  // that a head's K/V stays in one L2.  When that range is whole heads (lpt),
+  // the XCD walks it tile-major instead: the last (for causal rows the
+  // heaviest) tile of every head first, which evens out the finish times of
+  // its CUs on diagonal blocks.
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+  int w = x * p.per_xcd + j;
+  if (p.lpt) {
+    const int nb = p.per_xcd / p.n_qtiles;  // heads per XCD
+    w = (x * nb + j % nb) * p.n_qtiles + j / nb;
+  }
   if (w >= p.n_work) return false;
   const int qt_rev = w % p.n_qtiles;
   int rest = w / p.n_qtiles;

@@ -203,6 +203,13 @@ int check_step(const ra_step_desc* d, const void* q, const void* k, const void* 
 
 // Builds the kernel parameters of one step.  Returns false when nothing has to
 // be launched (empty rows, or ACCUM with every pair masked).
+// Work items per XCD, and whether each XCD's share is whole heads (then its
+// items run heaviest tile first).
+void set_grid(ra::StepParams* p) {
+  p->per_xcd = (p->n_work + 7) / 8;
+  p->lpt = (p->n_work % 8 == 0 && p->n_qtiles > 0 && p->per_xcd % p->n_qtiles == 0) ? 1 : 0;
+}
+
 bool build_params(const ra_step_desc* d, const void* q, const void* k, const void* v, float* o,
                   float* lse, bool accum, ra::StepParams* p, const ra_mask* m = nullptr) {
   if (d->Sq == 0) return false;
@@ -257,7 +264,7 @@ bool build_params(const ra_step_desc* d, const void* q, const void* k, const voi
   p->qt_span0 = (int)((p->qs_len[0] + bq - 1) / bq);
   p->n_qtiles = p->qt_span0 + (int)((p->qs_len[1] + bq - 1) / bq);
   p->n_work = p->B * p->Hq * p->n_qtiles;
-  p->per_xcd = (p->n_work + 7) / 8;
+  set_grid(p);
   return true;
 }
 
@@ -491,7 +498,7 @@ int ra_rank_backward_masked(const ra_rank_desc* d, const ra_mask* m, const void*
     bp.s.qt_span0 = (int)((bp.s.qs_len[0] + ra::kBwdRows - 1) / ra::kBwdRows);
     bp.s.n_qtiles = bp.s.qt_span0 + (int)((bp.s.qs_len[1] + ra::kBwdRows - 1) / ra::kBwdRows);
     bp.s.n_work = bp.s.B * bp.s.Hq * bp.s.n_qtiles;
-    bp.s.per_xcd = (bp.s.n_work + 7) / 8;
+    set_grid(&bp.s);
     bp.dout = dout;
     bp.lse = lse;
     bp.delta = delta;

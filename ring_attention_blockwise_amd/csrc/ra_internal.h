@@ -42,6 +42,7 @@ struct StepParams {
   int n_qtiles;             // query tiles per (batch, head)
   int n_work;               // B * Hq * n_qtiles
   int per_xcd;              // ceil(n_work / 8)
+  int lpt;                  // 1: each XCD's items are whole heads, walked heaviest tile first across them
 };
 
 // dtype: 0 = f32, 1 = bf16; D in {64, 128}.  The work decomposition of p
