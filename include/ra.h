@@ -177,9 +177,9 @@ typedef struct ra_mask {
  * ra_rank_forward_masked -- ra_rank_forward with a sliding window and/or
  * packed sequences.  Tiles the mask hides are not visited; a step whose
  * whole block is hidden is not launched; rows with no visible key in a step
- * keep the merge identity.  m == NULL is ra_rank_forward.  bf16 only
- * (RA_E_UNSUPPORTED for float32 inputs with a mask).  Both copies of the
- * boundaries must stay unchanged until the work completes.
+ * keep the merge identity.  m == NULL is ra_rank_forward.  Both dtypes.
+ * Both copies of the boundaries must stay unchanged until the work
+ * completes.
  */
 int ra_rank_forward_masked(const ra_rank_desc* d, const ra_mask* m,
                            const void* q_local, const void* k_shards,

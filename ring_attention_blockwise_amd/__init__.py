@@ -234,7 +234,7 @@ def ra_rank_forward_masked(q_local, k_shards, v_shards, o, lse, *, S: int, P: in
                            stream=None) -> None:
     """ra_rank_forward with a sliding window (``window`` > 0, causal) and/or
     packed sequences (``cu_seqlens``: boundaries 0 = c_0 < ... < c_n = S, a
-    sequence of ints).  bf16 inputs."""
+    sequence of ints).  bf16 or float32 inputs."""
     torch = _torch()
     _require(q_local, "q_local", ndim=4)
     _require(k_shards, "k_shards", dtype=q_local.dtype, ndim=5)

@@ -96,14 +96,28 @@ struct WaveState {
   float m_ref, l_part;
 };
 
+__device__ inline KTile ktile(const TileCursor& c) {
+  KTile kt;
+  kt.local0 = c.local0;
+  kt.glob0 = c.glob0;
+  kt.count = c.count();
+  return kt;
+}
+
+// Tile t of the plan (cursor cur) from buffer PAR; the lane's row sees keys
+// [row_lo, row_hi] (global positions).
 template <int D, int PAR>
 __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const TilePlan& tp, TileStage<D>& st,
-                                 const WorkItem& wi, int t, RA_LDS char* const* kbuf, RA_LDS char* const* vbuf,
-                                 long long qg, int lane) {
+                                 const WorkItem& wi, TileCursor& cur, int t, RA_LDS char* const* kbuf,
+                                 RA_LDS char* const* vbuf, long long row_lo, long long row_hi, int lane) {
   typedef Layout<D> Ly;
-  const KTile ti = tp.tile(t);
+  const TileCursor ci = cur;
+  const KTile ti = ktile(ci);
   const bool more = t + 1 < tp.n;
-  if (more) st.load(p, wi, tp.tile(t + 1));
+  if (more) {
+    cur.advance(tp);
+    st.load(p, wi, ktile(cur));
+  }
 
   const int L = lane >> 5;
   f32x16 s = {};
@@ -115,13 +129,15 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
       s = __builtin_amdgcn_mfma_f32_32x32x2f32(a, ws.q[u], s, 0, 0, 0);
     }
   }
-  if (t >= tp.n_full) {  // masked tiles only (a uniform branch)
-    int lim = ti.count;
-    if (p.causal) lim = (int)max(0LL, min((long long)lim, qg - ti.glob0 + 1));
+  if (ci.masked()) {  // masked tiles only (a uniform branch)
+    // keys [lo, lim) of the tile: the causal diagonal, a span's ragged end,
+    // a window's or a packed sequence's edges
+    const int lim = (int)max(0LL, min((long long)ti.count, row_hi - ti.glob0 + 1));
+    const int lo = (int)max(0LL, min((long long)kBK, row_lo - ti.glob0));
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = 8 * (r >> 2) + 4 * L + (r & 3);
-      if (key >= lim) s[r] = kNegInf;
+      if (key >= lim || key < lo) s[r] = kNegInf;
     }
   }
   float tmax = kNegInf;
@@ -192,11 +208,16 @@ void attn_step_f32_kernel(StepParams p) {
   const int wrow = 32 * wave + (lane & 31);
   const bool row_ok = wrow < wi.qrows;
   const long long qg = wi.qglob0 + wrow;
+  // the row's visible keys (any position: past the work item's rows the
+  // values are not used)
+  const long long row_lo = key_lo(p, qg), row_hi = key_hi(p, qg);
   const long long orow = ((long long)wi.b * p.Sq + wi.qlocal0 + wrow) * p.Hq + wi.h;  // (b, row, h)
 
   TileStage<D> st;
   st.init(p);
-  st.load(p, wi, tp.tile(0));
+  TileCursor cur;
+  cur.first(tp);
+  st.load(p, wi, ktile(cur));
   WaveState<D> ws;
   {
     const float* qrow = (const float*)p.q + orow * D;
@@ -214,10 +235,10 @@ void attn_step_f32_kernel(StepParams p) {
   // parity t mod 2
   int t = 0;
   for (; t + 1 < tp.n; t += 2) {
-    step_tile<D, 0>(ws, p, tp, st, wi, t, kbuf, vbuf, qg, lane);
-    step_tile<D, 1>(ws, p, tp, st, wi, t + 1, kbuf, vbuf, qg, lane);
+    step_tile<D, 0>(ws, p, tp, st, wi, cur, t, kbuf, vbuf, row_lo, row_hi, lane);
+    step_tile<D, 1>(ws, p, tp, st, wi, cur, t + 1, kbuf, vbuf, row_lo, row_hi, lane);
   }
-  if (t < tp.n) step_tile<D, 0>(ws, p, tp, st, wi, t, kbuf, vbuf, qg, lane);
+  if (t < tp.n) step_tile<D, 0>(ws, p, tp, st, wi, cur, t, kbuf, vbuf, row_lo, row_hi, lane);
 
   finish_rows<D, 1>(p, ws.o, 0, ws.m_ref, ws.l_part, row_ok, orow, lane);
 }

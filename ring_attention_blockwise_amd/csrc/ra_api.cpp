@@ -365,8 +365,6 @@ int ra_rank_forward_masked(const ra_rank_desc* d, const ra_mask* m, const void* 
   if (rc) return rc;
   rc = check_mask(m, d->S, d->causal != 0);
   if (rc) return rc;
-  if (m && (m->window > 0 || m->n_seqs > 0) && d->dtype != RA_DTYPE_BF16)
-    return fail(RA_E_UNSUPPORTED, "sliding-window and packed-sequence masks are built for bf16");
   const int64_t s_loc = d->S / d->P;
   const size_t esz = d->dtype == RA_DTYPE_BF16 ? 2 : 4;
   // Validate every step's descriptor before the first launch.

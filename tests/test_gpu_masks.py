@@ -69,6 +69,40 @@ def test_small_rings_every_row(ra, cfg):
         assert_close(o, lse, o_ref, l_ref, "bf16", f"{label} rank {r}")
 
 
+F32_CASES = [
+    # (label, B, Hq, Hkv, D, S, P, order, causal, window, cu): float32 inputs,
+    # the float32 kernel's tiles (ragged tails, both key-span edges)
+    ("f32_window50_contig_p4", 1, 2, 2, 64, 512, 4, "contiguous", True, 50, None),
+    ("f32_window7_zigzag_p4", 1, 4, 2, 64, 512, 4, "zigzag", True, 7, None),
+    ("f32_packed_zigzag_p4", 1, 2, 1, 64, 512, 4, "zigzag", True, 0, [0, 77, 78, 300, 512]),
+    ("f32_packed_noncausal_p2", 2, 2, 2, 64, 256, 2, "contiguous", False, 0, [0, 31, 200, 256]),
+    ("f32_packed_window_d128", 1, 2, 2, 128, 384, 3, "zigzag", True, 40, [0, 100, 250, 384]),
+]
+
+
+@pytest.mark.parametrize("cfg", F32_CASES, ids=[c[0] for c in F32_CASES])
+def test_f32_small_rings_every_row(ra, cfg):
+    """The masks through the float32 kernel, every row of every rank, to the
+    float32 tolerance."""
+    label, B, Hq, Hkv, D, S, P, order, causal, window, cu = cfg
+    case = RankCase(660 + len(label), "f32", B, Hq, Hkv, D, S, P, order, causal)
+    for r in range(P):
+        say(label, "rank", r)
+        o, lse = run_masked(ra, case, r, window, cu)
+        o_ref, l_ref = reference(case, r, window, cu)
+        assert_close(o, lse, o_ref, l_ref, "f32", f"{label} rank {r}")
+
+
+def test_f32_no_mask_equals_the_ring(ra):
+    """The float32 kernel's masked entry with no mask gives the plain ring's
+    bits."""
+    case = RankCase(641, "f32", 1, 2, 2, 64, 512, 4, "contiguous", True)
+    o_m, l_m = run_masked(ra, case, 3, 0, None)
+    o_r, l_r = case.run_rank(ra, 3)
+    np.testing.assert_array_equal(o_m, o_r)
+    np.testing.assert_array_equal(l_m, l_r)
+
+
 def test_no_mask_equals_the_ring(ra):
     """With neither a window nor packed sequences the masked driver is the
     plain one, bit for bit."""
