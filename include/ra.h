@@ -213,19 +213,21 @@ int ra_allgather_forward(const ra_rank_desc* d, const void* q_local,
  *   P = exp(scale q K^T - L),  dP = dO V^T,  delta = rowsum(dO * O),
  *   dS = P * (dP - delta),  dQ = scale dS K,  dK += scale dS^T Q,  dV += P^T dO,
  * with L and O the forward's final log-sum-exp and output.
- *   q_local   [B, S/P, Hq, D]        bf16, this rank's queries (local order)
- *   k_shards, v_shards [P, B, S/P, Hkv, D]  bf16, as for ra_rank_forward
+ *   q_local   [B, S/P, Hq, D]        this rank's queries (local order)
+ *   k_shards, v_shards [P, B, S/P, Hkv, D]  as for ra_rank_forward
  *   o         [B, S/P, Hq, D] float32, lse [B, S/P, Hq] float32 (ra_rank_forward's)
- *   dout      [B, S/P, Hq, D]        bf16, the loss gradient of o
+ *   dout      [B, S/P, Hq, D]        the loss gradient of o (q's dtype)
  *   dq        [B, S/P, Hq, D] float32: written
  *   dk_shards, dv_shards [P, B, S/P, Hkv, D] float32: ADDED to (the caller
  *             zeroes them; running every rank into the same buffers gives the
  *             full gradients)
  *   delta     [B, S/P, Hq] float32: caller-provided workspace, written with
  *             rowsum(dout * o)
- * Built for bf16 with D = 128 (RA_E_UNSUPPORTED otherwise); other
- * requirements as for ra_rank_forward.  Work is enqueued on `stream`: per
- * launched step one dQ kernel, then one dK/dV kernel.
+ * bf16 inputs with D = 128 run the tuned MFMA kernels (P and dS rounded to
+ * bf16 before their products); float32 inputs, or D = 64, run plain SIMT
+ * kernels in float32, meant for parity-scale problems.  Other requirements
+ * as for ra_rank_forward.  Work is enqueued on `stream`: per launched step
+ * a dQ kernel, then the dK/dV kernels.
  */
 int ra_rank_backward(const ra_rank_desc* d, const void* q_local,
                      const void* k_shards, const void* v_shards,

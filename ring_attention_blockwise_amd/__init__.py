@@ -302,8 +302,8 @@ def ra_allgather_forward(q_local, k_global, v_global, o, lse, *, S: int, P: int,
 def ra_rank_backward(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_shards, delta, *,
                      S: int, P: int, rank: int, order: str, causal: bool, scale: float | None = None,
                      stream=None) -> None:
-    """Backward of rank ``rank``'s ring attention (bf16, D = 128).  q_local,
-    dout [B, S/P, Hq, D] bf16; k_shards, v_shards [P, B, S/P, Hkv, D] bf16; o,
+    """Backward of rank ``rank``'s ring attention.  q_local, dout
+    [B, S/P, Hq, D]; k_shards, v_shards [P, B, S/P, Hkv, D] (one dtype); o,
     lse from ra_rank_forward.  dq [B, S/P, Hq, D] float32 is written;
     dk_shards, dv_shards [P, B, S/P, Hkv, D] float32 are added to; delta
     [B, S/P, Hq] float32 is workspace (written with rowsum(dout * o))."""

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libra.so")
-SOURCES = ["ra_api.cpp", "attn_step.hip", "attn_step_bf16.hip", "attn_bwd_bf16.hip", "merge_relayout.hip"]
+SOURCES = ["ra_api.cpp", "attn_step.hip", "attn_step_bf16.hip", "attn_bwd_bf16.hip", "attn_bwd_simt.hip",
+           "merge_relayout.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are turned off for all device code.  Code

@@ -365,16 +365,6 @@ __device__ inline bool decode_kv(const BwdParams& bp, KvItem& it) {
   return true;
 }
 
-// Rows of a query span that see some key of [k0, k1] (global positions):
-// key_hi and key_lo never decrease along the rows, so they are the rows t
-// with key_hi(t) >= k0 and key_lo(t) <= k1, one interval [t0, t1].
-__device__ inline void rows_seeing(const StepParams& p, long long k0, long long k1, long long& t0, long long& t1) {
-  t0 = p.causal ? k0 : (p.cu ? p.cu[seg_of(p, k0)] : 0);
-  t1 = 0x3fffffffffffffffLL;
-  if (p.window > 0) t1 = k1 + p.window - 1;
-  if (p.cu) t1 = min(t1, p.cu[seg_of(p, k1) + 1] - 1);
-}
-
 __device__ inline QPlan plan_q(const StepParams& p, long long kglob0, int kcount) {
   QPlan qp;
   qp.per_head = 0;

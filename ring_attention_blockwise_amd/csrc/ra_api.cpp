@@ -448,8 +448,6 @@ int ra_rank_backward_masked(const ra_rank_desc* d, const ra_mask* m, const void*
   if (!d) return fail(RA_E_INVAL, "descriptor is NULL");
   int rc = check_ring(d->order, d->S, d->P, d->rank);
   if (rc) return rc;
-  if (d->dtype != RA_DTYPE_BF16 || d->D != 128)
-    return fail(RA_E_UNSUPPORTED, "the backward pass is built for bf16 with D = 128");
   rc = check_mask(m, d->S, d->causal != 0);
   if (rc) return rc;
   const int64_t s_loc = d->S / d->P;
@@ -480,7 +478,10 @@ int ra_rank_backward_masked(const ra_rank_desc* d, const ra_mask* m, const void*
       hipDeviceGetAttribute(&n_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return fail(RA_E_HIP, "cannot query the device's compute units");
   const int64_t rows = (int64_t)d->B * s_loc * d->Hq;
-  hipError_t e = ra::launch_bwd_delta(rows, d->D, 1, dout, o, delta, (hipStream_t)stream);
+  // bf16 with D = 128: the tuned kernels; float32 or D = 64: the SIMT ones
+  const bool tuned = d->dtype == RA_DTYPE_BF16 && d->D == 128;
+  hipError_t e = tuned ? ra::launch_bwd_delta(rows, d->D, 1, dout, o, delta, (hipStream_t)stream)
+                       : ra::launch_simt_delta(rows, d->D, d->dtype, dout, o, delta, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RA_E_HIP, "delta launch failed: %s", hipGetErrorString(e));
   const int64_t shard_elems = (int64_t)d->B * s_loc * d->Hkv * d->D;
   for (int32_t s = 0; s < d->P; ++s) {
@@ -488,8 +489,9 @@ int ra_rank_backward_masked(const ra_rank_desc* d, const ra_mask* m, const void*
     const Spans ks = rank_spans(d->order, d->S, d->P, src);
     sd.n_kspans = ks.n;
     for (int i = 0; i < 2; ++i) sd.kspans[i] = i < ks.n ? ks.s[i] : ra_span{0, 0};
-    const char* kp = (const char*)k_shards + (size_t)src * shard_elems * 2;
-    const char* vp = (const char*)v_shards + (size_t)src * shard_elems * 2;
+    const size_t esz = d->dtype == RA_DTYPE_BF16 ? 2 : 4;
+    const char* kp = (const char*)k_shards + (size_t)src * shard_elems * esz;
+    const char* vp = (const char*)v_shards + (size_t)src * shard_elems * esz;
     ra::BwdParams bp;
     if (!build_params(&sd, q_local, kp, vp, nullptr, nullptr, s > 0, &bp.s, m)) continue;
     // the dQ kernel's query tiles are kBwdRows rows
@@ -515,7 +517,8 @@ int ra_rank_backward_masked(const ra_rank_desc* d, const ra_mask* m, const void*
     // heaviest workgroup.
     const KvLoad kl = kv_load(bp.s, m);
     bp.kv_split = ((int64_t)bp.s.B * bp.s.Hkv * kl.active <= n_cus || 2 * kl.max * kl.active >= 3 * kl.total) ? 1 : 0;
-    e = ra::launch_attn_bwd_bf16(bp, (hipStream_t)stream);
+    e = tuned ? ra::launch_attn_bwd_bf16(bp, (hipStream_t)stream)
+              : ra::launch_attn_bwd_simt(bp, d->dtype, d->D, (hipStream_t)stream);
     if (e != hipSuccess) return fail(RA_E_HIP, "backward launch failed: %s", hipGetErrorString(e));
   }
   return ok();

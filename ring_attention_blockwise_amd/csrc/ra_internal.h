@@ -75,6 +75,10 @@ struct BwdParams {
 };
 
 hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s);
+// The same step for float32 inputs (dtype 0) or D = 64: plain SIMT kernels.
+hipError_t launch_attn_bwd_simt(const BwdParams& p, int dtype, int D, hipStream_t s);
+hipError_t launch_simt_delta(long long rows, int D, int dtype, const void* dout, const float* o, float* delta,
+                             hipStream_t s);
 // delta[row] = sum_d dO[row, d] * O[row, d] over rows of D elements; dO bf16
 // (dtype 1) or f32 (dtype 0), O f32.
 hipError_t launch_bwd_delta(long long rows, int D, int dtype, const void* dout, const float* o, float* delta,

@@ -95,6 +95,51 @@ def test_small_rings_all_ranks(ra, cfg):
         assert e_q <= GRAD_TOL and e_k <= GRAD_TOL and e_v <= GRAD_TOL
 
 
+# Float32 inputs or D = 64 take the plain SIMT backward (float32 throughout,
+# no bf16 rounding of P or dS): float32 inputs to 1e-5 of the gradient scale
+# (observed <= 1.3e-6), bf16 inputs to the bf16 bound.
+SIMT_TOL = {"f32": 1e-5, "bf16": GRAD_TOL}
+
+SIMT = [
+    # (label, dtype, B, Hq, Hkv, D, S, P, order, causal)
+    ("f32_mha2_d64_s512_ring4_contig", "f32", 1, 2, 2, 64, 512, 4, "contiguous", True),
+    ("f32_gqa_d128_zigzag_p4", "f32", 1, 4, 2, 128, 512, 4, "zigzag", True),
+    ("f32_noncausal_b2_d64", "f32", 2, 2, 1, 64, 256, 2, "contiguous", False),
+    ("bf16_gqa_d64_zigzag_p4", "bf16", 1, 8, 2, 64, 1024, 4, "zigzag", True),
+]
+
+
+@pytest.mark.parametrize("cfg", SIMT, ids=[c[0] for c in SIMT])
+def test_simt_rings_all_ranks(ra, cfg):
+    """Float32 inputs and D = 64: every rank's backward into shared dK/dV
+    against the oracle's gradients of the whole sequence."""
+    import torch
+    label, dtype, B, Hq, Hkv, D, S, P, order, causal = cfg
+    case = BwdCase(320 + len(label), dtype, B, Hq, Hkv, D, S, P, order, causal)
+    s_loc = S // P
+    dk = torch.zeros((P, B, s_loc, Hkv, D), device="cuda")
+    dv = torch.zeros_like(dk)
+    dqs = []
+    for r in range(P):
+        say(label, "backward rank", r)
+        dqs.append(case.run_backward(ra, r, dk, dv))
+    Qg = si.to_f64(case.q_rows([(0, S)]), dtype)
+    Kg, Vg = si.to_f64(case.Kg, dtype), si.to_f64(case.Vg, dtype)
+    dOg = si.to_f64(case.dout_rows([(0, S)]), dtype)
+    dQ, dK, dV = ob.attention_grads(Qg, Kg, Vg, dOg, causal, case.scale)
+    dkh, dvh = dk.cpu().numpy(), dv.cpu().numpy()
+    tol = SIMT_TOL[dtype]
+    for r in range(P):
+        pos = im.rank_positions(S, P, r, order)
+        e_q = _rel_err(dqs[r], dQ[:, pos])
+        e_k = _rel_err(dkh[r], dK[:, pos])
+        e_v = _rel_err(dvh[r], dV[:, pos])
+        say(f"{label} rank {r}: rel err dQ {e_q:.2e} dK {e_k:.2e} dV {e_v:.2e}")
+        assert np.isfinite(dqs[r]).all() and np.isfinite(dkh[r]).all() and np.isfinite(dvh[r]).all()
+        assert e_q <= tol and e_k <= tol and e_v <= tol
+    case.release()
+
+
 @pytest.mark.parametrize("which", ["first", "last"])
 def test_full_size_131k_sampled_and_conserved(ra, which):
     """131k-token zigzag ring of 16, GQA 32/8: dQ of sampled rows against the

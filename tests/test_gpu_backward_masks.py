@@ -119,6 +119,37 @@ def test_small_rings_all_ranks(ra, cfg):
     case.release()
 
 
+F32_CASES = [
+    # (label, D, B, Hq, Hkv, S, P, order, causal, window, cu): the SIMT backward
+    ("f32_window40_zigzag_p4", 64, 1, 2, 2, 512, 4, "zigzag", True, 40, None),
+    ("f32_packed_window_contig_p4", 64, 1, 4, 2, 512, 4, "contiguous", True, 30, [0, 100, 101, 400, 512]),
+    ("f32_packed_noncausal_d128", 128, 1, 2, 1, 256, 2, "contiguous", False, 0, [0, 90, 256]),
+]
+
+
+@pytest.mark.parametrize("cfg", F32_CASES, ids=[c[0] for c in F32_CASES])
+def test_f32_masked_rings_all_ranks(ra, cfg):
+    """The masks through the float32 (SIMT) backward, to 1e-5."""
+    import torch
+    label, D, B, Hq, Hkv, S, P, order, causal, window, cu = cfg
+    case = MaskedBwdCase(540 + len(label), "f32", B, Hq, Hkv, D, S, P, order, causal, window=window, cu=cu)
+    s_loc = S // P
+    dk = torch.zeros((P, B, s_loc, Hkv, D), device="cuda")
+    dv = torch.zeros_like(dk)
+    dqs = [case.run_backward(ra, r, dk, dv) for r in range(P)]
+    Qg = si.to_f64(case.q_rows([(0, S)]), "f32")
+    Kg, Vg = si.to_f64(case.Kg, "f32"), si.to_f64(case.Vg, "f32")
+    dOg = si.to_f64(case.dout_rows([(0, S)]), "f32")
+    dQ, dK, dV = ob.attention_grads(Qg, Kg, Vg, dOg, causal, case.scale, window=window, cu_seqlens=cu)
+    dkh, dvh = dk.cpu().numpy(), dv.cpu().numpy()
+    for r in range(P):
+        pos = im.rank_positions(S, P, r, order)
+        e = [_rel_err(dqs[r], dQ[:, pos]), _rel_err(dkh[r], dK[:, pos]), _rel_err(dvh[r], dV[:, pos])]
+        say(f"{label} rank {r}: rel err dQ {e[0]:.2e} dK {e[1]:.2e} dV {e[2]:.2e}")
+        assert max(e) <= 1e-5
+    case.release()
+
+
 def test_no_mask_equals_unmasked_backward(ra):
     """With neither a window nor boundaries the masked entry point is
     ra_rank_backward: the same kernels, so the same bits."""
