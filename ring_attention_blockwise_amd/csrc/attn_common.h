@@ -265,7 +265,9 @@ struct WorkItem {
 template <int BQ>
 __device__ inline bool decode_work(const StepParams& p, WorkItem& wi) {
   // Workgroup i runs on XCD i mod 8; XCD x takes items [x per_xcd,
-  // (x+1) per_xcd) of the list (heads outer, query tiles last first), so
+  // (x+1) per_xcd) of the list (heads outer, then query tiles, heaviest end
+  // first: the last tiles for causal rows, the first ones when the host finds
+  // them heavier, as for a window over an earlier block), so
   // that a head's K/V stays in one L2.  When that range is whole heads (lpt),
   // the XCD walks it tile-major instead: the last (for causal rows the
   // heaviest) tile of every head first, which evens out the finish times of
@@ -284,7 +286,7 @@ __device__ inline bool decode_work(const StepParams& p, WorkItem& wi) {
   wi.g = rest % p.Hkv;
   wi.b = rest / p.Hkv;
   wi.h = wi.g * p.G + hh;
-  const int qt = p.n_qtiles - 1 - qt_rev;
+  const int qt = p.first_heavy ? qt_rev : p.n_qtiles - 1 - qt_rev;
   const int qs = qt < p.qt_span0 ? 0 : 1;
   const long long q_in = (long long)(qs ? qt - p.qt_span0 : qt) * BQ;
   wi.qrows = (int)min((long long)BQ, p.qs_len[qs] - q_in);

@@ -203,6 +203,19 @@ int check_step(const ra_step_desc* d, const void* q, const void* k, const void* 
 
 // Builds the kernel parameters of one step.  Returns false when nothing has to
 // be launched (empty rows, or ACCUM with every pair masked).
+// Keys of the step's key spans that the query at global position t sees.
+int64_t visible_keys(const ra::StepParams& p, const ra_mask* m, int64_t t) {
+  const int64_t lo = m ? host_key_lo(m, t) : 0;
+  const int64_t hi = m ? host_key_hi(m, p.causal != 0, t) : (p.causal ? t : INT64_MAX);
+  int64_t n = 0;
+  for (int s = 0; s < p.nks; ++s) {
+    const int64_t a = std::max(lo, (int64_t)p.ks_start[s]);
+    const int64_t b = std::min(hi, (int64_t)(p.ks_start[s] + p.ks_len[s] - 1));
+    if (a <= b) n += b - a + 1;
+  }
+  return n;
+}
+
 // Work items per XCD, and whether each XCD's share is whole heads (then its
 // items run heaviest tile first).
 void set_grid(ra::StepParams* p) {
@@ -258,6 +271,17 @@ bool build_params(const ra_step_desc* d, const void* q, const void* k, const voi
     off += qs.len;
   }
   if (p->nqs == 0) return false;
+  {
+    // which end of the query rows sees more keys: the first tile's or the
+    // last tile's (each by its first and last row)
+    const int bq = ra::step_rows(d->dtype);
+    const int64_t f0 = p->qs_start[0], f1 = f0 + std::min((int64_t)bq, (int64_t)p->qs_len[0]) - 1;
+    const int ls = p->nqs - 1;
+    const int64_t l1 = p->qs_start[ls] + p->qs_len[ls] - 1, l0 = std::max((int64_t)p->qs_start[ls], l1 - bq + 1);
+    const int64_t wf = visible_keys(*p, m, f0) + visible_keys(*p, m, f1);
+    const int64_t wl = visible_keys(*p, m, l0) + visible_keys(*p, m, l1);
+    p->first_heavy = wf > wl ? 1 : 0;
+  }
   for (int i = p->nqs; i < 2; ++i) p->qs_start[i] = p->qs_len[i] = p->qs_off[i] = 0;
   for (int i = p->nks; i < 2; ++i) p->ks_start[i] = p->ks_len[i] = p->ks_off[i] = 0;
   const int bq = ra::step_rows(d->dtype);
