@@ -119,3 +119,35 @@ def test_one_hip_runtime_shared_with_torch():
     process would receive torch's streams and pointers and fail."""
     paths = ra.hip_runtime_path().split(";")
     assert len(paths) == 1, paths
+
+
+def _mask(window=0, cu=None, dev=None):
+    """An ra_mask (and the host array it points at, to keep alive)."""
+    host = (ctypes.c_int64 * len(cu))(*cu) if cu is not None else None
+    m = ra.ra_mask(window, len(cu) - 1 if cu is not None else 0,
+                   ctypes.cast(host, ctypes.POINTER(ctypes.c_int64)) if host is not None else None,
+                   FAKE if dev is None else dev)
+    return m, host
+
+
+@pytest.mark.parametrize("window,cu,dev,causal", [
+    (-1, None, None, 1),                   # negative window
+    (64, None, None, 0),                   # a window needs the causal mask
+    (0, [1, 2048, 4096], None, 1),         # boundaries must start at 0
+    (0, [0, 2048, 4000], None, 1),         # ... and end at S
+    (0, [0, 3000, 2048, 4096], None, 1),   # ... and increase
+    (0, [0, 2048, 4096], 4, 1),            # device copy not 8-byte aligned
+])
+@pytest.mark.parametrize("entry", ["forward", "backward"])
+def test_masked_entries_reject_bad_masks(window, cu, dev, causal, entry):
+    """Both masked entry points check the mask on the host before anything
+    is enqueued."""
+    d = ra.ra_rank_desc(1, 1, 8, 2, 128, 4096, 8, 0, 1, causal, 0.088)
+    m, _keep = _mask(window, cu, dev)
+    if entry == "forward":
+        rc = ra.lib.ra_rank_forward_masked(ctypes.byref(d), ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    else:
+        rc = ra.lib.ra_rank_backward_masked(ctypes.byref(d), ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == ra.RA_E_INVAL
+    assert ra.ra_last_error()
