@@ -25,10 +25,13 @@
 //     every query head of the group that see them: S = Q K^T (Q rows from
 //     LDS), then dV^T += dO^T P; or S and dP = dO V^T, then dK^T += Q^T dS,
 //     with dO^T, Q^T by transposing LDS reads.  Fused, the two need about 290
-//     registers (one wave per SIMD); split, 172 and 228 (two per SIMD), for
-//     one more product (S twice).  The softmax rows are spread over the
+//     registers (one wave per SIMD); split, about 155 and 210 (two per SIMD),
+//     for one more product (S twice).  The softmax rows are spread over the
 //     accumulator registers here, so the rows' L and delta come from LDS as 16
-//     values per lane.
+//     values per lane.  When a launch's key tiles carry very unequal work
+//     (causal, windowed diagonals), eight-wave workgroups let two groups of
+//     four waves share a key tile's query tiles; the second group hands its
+//     partial sums to the first through LDS.
 // Tiles are copied global -> LDS by buffer loads with the LDS bit.  One LDS
 // layout serves both read patterns: chunk c of row r sits at c ^ csw(r), with
 // csw(r) = 4 (r mod 4) + (r / 4) mod 4, which keeps the 16 rows of a row read
