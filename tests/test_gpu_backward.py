@@ -140,34 +140,32 @@ def test_simt_rings_all_ranks(ra, cfg):
     case.release()
 
 
-@pytest.mark.parametrize("which", ["first", "last"])
-def test_full_size_131k_sampled_and_conserved(ra, which):
-    """131k-token zigzag ring of 16, GQA 32/8: dQ of sampled rows against the
-    oracle, and over all keys dK sums to zero and dV to the sum of the rank's
-    dO (each row's weights sum to one, its dS to zero)."""
+def _full_size_check(ra, name, r, seed):
+    """Rank r of a full-size workload: dQ of sampled rows against the oracle,
+    and over all keys dK sums to zero and dV to the sum of the rank's dO (each
+    row's weights sum to one, its dS to zero)."""
     import torch
-    w = workload("bf16_gqa32x8_d128_s128k_ring16_zigzag_causal")
-    r = 0 if which == "first" else w.P - 1
+    w = workload(name)
     case = BwdCase.from_workload(w)
     s_loc = w.S // w.P
     dk = torch.zeros((w.P, w.B, s_loc, w.Hkv, w.D), device="cuda")
     dv = torch.zeros_like(dk)
-    say("backward full size rank", r)
+    say("backward full size", name, "rank", r)
     dq = case.run_backward(ra, r, dk, dv)
     assert np.isfinite(dq).all()
     spans = im.rank_spans(w.S, w.P, r, w.order)
     pos = im.rank_positions(w.S, w.P, r, w.order)
-    rng = np.random.default_rng(40 + r)
+    rng = np.random.default_rng(seed + r)
     rows = np.unique(np.concatenate([[0, 1, s_loc // 2 - 1, s_loc // 2, s_loc - 1],
                                      rng.choice(s_loc, 6, replace=False)]))
     qsel = pos[rows]
     q = si.to_f64(case.q_rows([(int(t), 1) for t in qsel]), "bf16")
     do = si.to_f64(case.dout_rows([(int(t), 1) for t in qsel]), "bf16")
-    kmax = int(qsel.max()) + 1
+    kmax = int(qsel.max()) + 1 if w.causal else w.S
     ref = ob.dq_rows(q, qsel, si.to_f64(case.Kg[:, :kmax], "bf16"), si.to_f64(case.Vg[:, :kmax], "bf16"), do,
-                     True, case.scale, kpos=np.arange(kmax))
+                     w.causal, case.scale, kpos=np.arange(kmax))
     e_q = _rel_err(dq[:, rows], ref)
-    say(f"full size rank {r}: sampled dQ rel err {e_q:.2e}")
+    say(f"{name} rank {r}: sampled dQ rel err {e_q:.2e}")
     assert e_q <= GRAD_TOL
     # conservation over every key of every shard
     dks = dk.sum(dim=(0, 2), dtype=torch.float64).cpu().numpy()       # [B, Hkv, D]
@@ -178,6 +176,23 @@ def test_full_size_131k_sampled_and_conserved(ra, which):
     scale_v = np.abs(want_v).max()
     e_v = float(np.abs(dvs - want_v).max() / scale_v)
     e_k = float(np.abs(dks).max() / scale_v)
-    say(f"full size rank {r}: sum dV rel err {e_v:.2e}, |sum dK| / |sum dO| {e_k:.2e}")
+    say(f"{name} rank {r}: sum dV rel err {e_v:.2e}, |sum dK| / |sum dO| {e_k:.2e}")
     assert e_v <= GRAD_TOL and e_k <= GRAD_TOL
     case.release()
+
+
+@pytest.mark.parametrize("which", ["first", "last"])
+def test_full_size_131k_sampled_and_conserved(ra, which):
+    """131k-token zigzag ring of 16, GQA 32/8, first and last rank."""
+    name = "bf16_gqa32x8_d128_s128k_ring16_zigzag_causal"
+    _full_size_check(ra, name, 0 if which == "first" else workload(name).P - 1, 40)
+
+
+@pytest.mark.parametrize("name,r", [
+    ("bf16_gqa32x8_d128_s32k_ring8_zigzag_causal", 3),
+    ("bf16_mha16_b2_d128_s64k_ring8_contiguous_full", 5),
+])
+def test_full_size_other_workloads(ra, name, r):
+    """The 32k zigzag ring of 8 and the non-causal contiguous ring of 8 (batch
+    2, 16 heads without grouping) at full size."""
+    _full_size_check(ra, name, r, 70)
