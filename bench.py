@@ -256,6 +256,47 @@ def time_window(ra, w, rank, window, reps=5):
             "frac_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def time_graph(ra, name, rank, reps=20):
+    """A smaller ring, eager against HIP-graph replay: the 32k-token zigzag
+    ring of 8 (about 0.1 ms of work per step) captured once as a graph of its
+    launches (the library allocates nothing and records no memset)."""
+    import torch
+    from seeded_inputs import workload
+    w = workload(name)
+    q, ks, vs, o, lse = build_inputs(ra, w, rank)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    kw = dict(S=w.S, P=w.P, rank=rank, order=w.order, causal=w.causal, scale=w.scale, stream=stream)
+
+    def eager():
+        ra.ra_rank_forward(q, ks, vs, o, lse, **kw)
+
+    res = {}
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            eager()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            eager()
+        for mode, run in (("eager", eager), ("graph", g.replay)):
+            run()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                run()
+            b.record(stream)
+            b.synchronize()
+            res[mode] = a.elapsed_time(b) / reps
+    torch.cuda.synchronize()
+    flops = algorithmic_flops(w, rank)
+    del q, ks, vs, o, lse, g
+    torch.cuda.empty_cache()
+    return {"kernel": "rank_forward_32k_graph", "workload": name, "ms": res["graph"], "eager_ms": res["eager"],
+            "TFLOP/s": flops / (res["graph"] * 1e-3) / 1e12,
+            "eager_TFLOP/s": flops / (res["eager"] * 1e-3) / 1e12,
+            "frac_peak": flops / (res["graph"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def time_merge(ra, rows, D, reps=20):
     """Standalone merge, rotating buffer sets so the working set exceeds the
     256 MB Infinity Cache."""
@@ -473,6 +514,8 @@ def main():
         if w.dtype == "bf16" and w.D == 128:
             aux.append(time_backward(ra, w, rank))
             aux.append(time_backward(ra, w, rank, window=4096))
+        if w.dtype == "bf16":
+            aux.append(time_graph(ra, "bf16_gqa32x8_d128_s32k_ring8_zigzag_causal", 0))
         aux.append(time_merge(ra, w.B * (w.S // w.P) * w.Hq, w.D))
         aux.append(time_relayout(ra, 2, 8192, 16, 128, 8))
         aux.extend(time_ulysses_pieces(ra, 2, 8192, 16, 128, 8))
