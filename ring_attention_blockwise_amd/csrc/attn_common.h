@@ -247,6 +247,21 @@ struct TileCursor {
     for (int j = 1; j < 6; ++j)
       if (j > seg && enter(tp, j)) return;
   }
+  // tile idx (< tp.n) of the plan order
+  __device__ void seek(const TilePlan& tp, int idx) {
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      if (!enter(tp, j)) continue;
+      if (idx < rem) {
+        rem -= idx;
+        local0 += (long long)idx * kBK;
+        glob0 += (long long)idx * kBK;
+        vis -= (long long)idx * kBK;
+        return;
+      }
+      idx -= rem;
+    }
+  }
 };
 
 // ---------------------------------------------------------------------------

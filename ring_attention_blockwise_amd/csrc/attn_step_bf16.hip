@@ -28,6 +28,10 @@
 //     per-lane DMA offsets are computed once per work item.
 //   * Only key tiles with at least one visible key are visited; tiles all of
 //     whose keys every row of the work item sees run first and skip the mask.
+//   * Steps with fewer work items than two per CU (small rings) run a
+//     second kernel: eight-wave workgroups whose two wave sets take the two
+//     halves of an item's key tiles and merge their partial softmax sums
+//     through LDS at the end, so every SIMD still interleaves two waves.
 //
 // Per-wave math (64 queries x 32 keys per tile)
 //   S^T = K Q^T on 32x32x16 MFMAs.  Lane l feeds the K row sigma(l % 32),
@@ -49,6 +53,7 @@ namespace {
 using namespace dev;
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kQB = 2;         // 32-row query blocks per wave
@@ -172,23 +177,32 @@ __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "mem
 // Iteration t.  PAR = t mod 2 names the LDS buffers statically: tile t is read
 // from kbuf[PAR] / vbuf[PAR]; tile t+1 is started first, into kbuf[PAR ^ 1] /
 // vbuf[PAR ^ 1].
-template <int D, int PAR, bool kExt>
+// Tile t of the plan from buffer PAR while tile t+1 is copied into PAR ^ 1.
+// te: end of this wave group's tiles (a tile at or past it only keeps the
+// group in step with the other at the barrier); phase: 0 or 1, which of the
+// two wave sets sharing each SIMD this is.
+template <int D, int PAR, bool kExt, bool kKS>
 __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const TilePlan& tp, const WorkItem& wi,
-                                 const Stager<D>& st, TileCursor& cur, int t, RA_LDS char* const* kbuf,
-                                 RA_LDS char* const* vbuf, const RA_LDS int* row_lo, const RA_LDS int* row_hi,
-                                 int lane, int wave) {
+                                 const Stager<D>& st, TileCursor& cur, int t, int te, unsigned phase,
+                                 RA_LDS char* const* kbuf, RA_LDS char* const* vbuf, const RA_LDS int* row_lo,
+                                 const RA_LDS int* row_hi, int lane, int wave) {
+  if (kKS && t >= te) {
+    __syncthreads();
+    return;
+  }
   const Lane<D> ln((unsigned)(p.Hkv * D * 2), wave);
   const TileCursor ti = cur;
-  // Two workgroups share each CU; the wave arbiter favours the older one,
-  // which then finishes its (equal) work long before the younger.  Swapping
-  // the issue priority every 32 tiles, in opposite phase for the first and
-  // second workgroup a CU receives (dispatch fills one slot on each of the
-  // 256 CUs before the second), lets both progress at about the same rate.
-  if ((((unsigned)t >> 5) ^ (blockIdx.x >> 8)) & 1u)
+  // Two wave sets share each SIMD (two workgroups of a CU, or the two groups
+  // of an eight-wave workgroup); the wave arbiter favours the older, which
+  // then finishes its (equal) work long before the younger.  Swapping the
+  // issue priority every 32 tiles, in opposite phase for the two (dispatch
+  // fills one slot on each of the 256 CUs before the second), lets both
+  // progress at about the same rate.
+  if ((((unsigned)t >> 5) ^ (kKS ? phase : (blockIdx.x >> 8))) & 1u)
     __builtin_amdgcn_s_setprio(1);
   else
     __builtin_amdgcn_s_setprio(0);
-  if (t + 1 < tp.n) {
+  if (t + 1 < (kKS ? te : tp.n)) {
     cur.advance(tp);
     st.issue(cur, kbuf[PAR ^ 1], vbuf[PAR ^ 1]);
   }
@@ -324,6 +338,57 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
   __syncthreads();
 }
 
+// One wave set's pass over tiles [tb, te) of the plan (iters iterations, the
+// same for both sets of an eight-wave workgroup): tile tb in flight while Q
+// is read, then the tiles through buffers kbuf, vbuf.
+template <int D, bool kExt, bool kKS>
+__device__ __attribute__((always_inline)) inline void fwd_pass(WaveState<D>& ws, const StepParams& p,
+                                                               const TilePlan& tp, const WorkItem& wi, int tb, int te,
+                                                               int iters, unsigned phase, RA_LDS char* const* kbuf,
+                                                               RA_LDS char* const* vbuf, const RA_LDS int* row_lo,
+                                                               const RA_LDS int* row_hi, int lane, int wave) {
+  Stager<D> st;
+  st.init(p, wi, Lane<D>((unsigned)(p.Hkv * D * 2), wave));
+  TileCursor cur;
+  cur.first(tp);
+  if (kKS && tb > 0) cur.seek(tp, tb);
+  if (!kKS || tb < te) st.issue(cur, kbuf[0], vbuf[0]);
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int wrow = 64 * wave + 32 * qb + (lane & 31);
+    const long long orow = ((long long)wi.b * p.Sq + wi.qlocal0 + wrow) * p.Hq + wi.h;  // (b, row, h)
+    const uint16_t* qrow = (const uint16_t*)p.q + orow * D;
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u)
+      ws.q[qb][u] = wrow < wi.qrows ? *(const bf16x8*)(qrow + 16 * u + 8 * (lane >> 5)) : bf16x8{};
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) ws.o[db][qb] = f32x16{};
+    ws.m_ref[qb] = kNegInf;
+    ws.l_part[qb] = 0.f;
+  }
+  wait_loads();
+  __syncthreads();
+
+  // main loop, unrolled by two so that buffers are named statically:
+  // iteration i uses parity i mod 2.
+  const int tend = kKS ? tb + iters : tp.n;
+  int t = kKS ? tb : 0;
+  for (; t + 1 < tend; t += 2) {
+    step_tile<D, 0, kExt, kKS>(ws, p, tp, wi, st, cur, t, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave);
+    step_tile<D, 1, kExt, kKS>(ws, p, tp, wi, st, cur, t + 1, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave);
+  }
+  if (t < tend)
+    step_tile<D, 0, kExt, kKS>(ws, p, tp, wi, st, cur, t, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave);
+}
+
+// The kernel above: four waves (256 query rows, 64 per wave) walk every key
+// tile of the work item; two workgroups per CU.  This one (kKS = true; the
+// template keeps the shared code paths in step with it): eight waves, two sets of four over the same 256 rows, the
+// first taking the first half of the item's key tiles and the second the
+// rest; at the end the second hands its (O, m, l) to the first through LDS,
+// which merges them (the softmax merge of two partial sums) and writes the
+// rows.  For steps with fewer work items than two per CU: one workgroup per
+// CU still keeps two waves on every SIMD.
 template <int D, bool kExt>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_step_bf16_kernel(StepParams p) {
@@ -386,10 +451,144 @@ void attn_step_bf16_kernel(StepParams p) {
   // iteration t uses parity t mod 2.
   int t = 0;
   for (; t + 1 < tp.n; t += 2) {
-    step_tile<D, 0, kExt>(ws, p, tp, wi, st, cur, t, kbuf, vbuf, row_lo, row_hi, lane, wave);
-    step_tile<D, 1, kExt>(ws, p, tp, wi, st, cur, t + 1, kbuf, vbuf, row_lo, row_hi, lane, wave);
+    step_tile<D, 0, kExt, false>(ws, p, tp, wi, st, cur, t, tp.n, 0u, kbuf, vbuf, row_lo, row_hi, lane, wave);
+    step_tile<D, 1, kExt, false>(ws, p, tp, wi, st, cur, t + 1, tp.n, 0u, kbuf, vbuf, row_lo, row_hi, lane,
+                                  wave);
   }
-  if (t < tp.n) step_tile<D, 0, kExt>(ws, p, tp, wi, st, cur, t, kbuf, vbuf, row_lo, row_hi, lane, wave);
+  if (t < tp.n) step_tile<D, 0, kExt, false>(ws, p, tp, wi, st, cur, t, tp.n, 0u, kbuf, vbuf, row_lo, row_hi, lane, wave);
+
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int wrow = 64 * wave + 32 * qb + (lane & 31);
+    const long long orow = ((long long)wi.b * p.Sq + wi.qlocal0 + wrow) * p.Hq + wi.h;
+    finish_rows<D, kQB>(p, ws.o, qb, ws.m_ref[qb], ws.l_part[qb], wrow < wi.qrows, orow, lane);
+  }
+}
+
+template <int D, bool kExt, bool kKS>
+__global__ __launch_bounds__(kKS ? 2 * kThreads : kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_step_bf16_ks_kernel(StepParams p) {
+  typedef Layout<D> Ly;
+  // the hand-over below puts 16 KB per wave and round into two tile buffers
+  static_assert(!kKS || (D == 128 && Ly::kKTileBytes == 8192 && Ly::kVTileBytes == 8192), "kKS needs D = 128");
+  constexpr int kT = kKS ? 2 * kThreads : kThreads;
+  __shared__ __attribute__((aligned(16))) char k0_raw[Ly::kKTileBytes];
+  __shared__ __attribute__((aligned(16))) char k1_raw[Ly::kKTileBytes];
+  __shared__ __attribute__((aligned(16))) char v0_raw[Ly::kVTileBytes];
+  __shared__ __attribute__((aligned(16))) char v1_raw[Ly::kVTileBytes];
+  __shared__ __attribute__((aligned(16))) char k2_raw[kKS ? Ly::kKTileBytes : 16];
+  __shared__ __attribute__((aligned(16))) char k3_raw[kKS ? Ly::kKTileBytes : 16];
+  __shared__ __attribute__((aligned(16))) char v2_raw[kKS ? Ly::kVTileBytes : 16];
+  __shared__ __attribute__((aligned(16))) char v3_raw[kKS ? Ly::kVTileBytes : 16];
+  __shared__ __attribute__((aligned(16))) float xm_raw[kKS ? 4 * 64 * 2 * kQB : 4];
+  __shared__ int lo_raw[kBQBf16], hi_raw[kBQBf16];
+  const RA_LDS int* row_lo = (const RA_LDS int*)lo_raw;
+  const RA_LDS int* row_hi = (const RA_LDS int*)hi_raw;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = kKS ? wv >> 2 : 0;
+  const int wave = wv & 3;
+
+  WorkItem wi;
+  if (!decode_work<kBQBf16>(p, wi)) return;
+  const TilePlan tp = plan_tiles(p, wi.qglob0, wi.qglob0 + wi.qrows - 1);
+  if (tp.n == 0) {
+    store_identity<D, kT>(p, wi);
+    return;
+  }
+
+  if (kExt) {
+    // visible key range of each row of the work item (window, packed
+    // sequences), relative to the item's first row and clamped to +-2^30
+    for (int r = threadIdx.x; r < kBQBf16; r += kT) {
+      const long long t = wi.qglob0 + r;
+      lo_raw[r] = (int)max(-(1LL << 30), min(1LL << 30, key_lo(p, t) - wi.qglob0));
+      hi_raw[r] = (int)max(-(1LL << 30), min(1LL << 30, key_hi(p, t) - wi.qglob0));
+    }
+  }
+
+  WaveState<D> ws;
+  const int half = kKS ? (tp.n + 1) / 2 : tp.n;
+  if (grp == 0) {
+    RA_LDS char* const kbuf[2] = {(RA_LDS char*)k0_raw, (RA_LDS char*)k1_raw};
+    RA_LDS char* const vbuf[2] = {(RA_LDS char*)v0_raw, (RA_LDS char*)v1_raw};
+    fwd_pass<D, kExt, kKS>(ws, p, tp, wi, 0, half, half, 0u, kbuf, vbuf, row_lo, row_hi, lane, wave);
+  } else {
+    RA_LDS char* const kbuf[2] = {(RA_LDS char*)k2_raw, (RA_LDS char*)k3_raw};
+    RA_LDS char* const vbuf[2] = {(RA_LDS char*)v2_raw, (RA_LDS char*)v3_raw};
+    fwd_pass<D, kExt, kKS>(ws, p, tp, wi, half, tp.n, half, 1u, kbuf, vbuf, row_lo, row_hi, lane, wave);
+  }
+
+  if (kKS) {
+    // The second set's partial sums to the first: its (m, l) per row into
+    // xm, its O in rounds of two 32-column blocks, 16 KB per wave per round,
+    // through the idle tile buffers (two per wave).  Exponents relative to
+    // each set's own reference m: O = a0 O0 + a1 O1, l = a0 l0 + a1 l1 with
+    // a = exp2((m_set - m) sl2) for m = max(m0, m1) (a set that saw no key
+    // has m = -inf and a = 0).
+    RA_LDS float* const xm = (RA_LDS float*)xm_raw + (wave * 64 + lane) * 2 * kQB;
+    float a0[kQB], a1[kQB];
+#pragma unroll
+    for (int r = 0; r < D / 64; ++r) {
+      RA_LDS char* const xb0 = wave == 0   ? (RA_LDS char*)k0_raw
+                               : wave == 1 ? (RA_LDS char*)v0_raw
+                               : wave == 2 ? (RA_LDS char*)k2_raw
+                                           : (RA_LDS char*)v2_raw;
+      RA_LDS char* const xb1 = wave == 0   ? (RA_LDS char*)k1_raw
+                               : wave == 1 ? (RA_LDS char*)v1_raw
+                               : wave == 2 ? (RA_LDS char*)k3_raw
+                                           : (RA_LDS char*)v3_raw;
+      if (grp == 1) {
+        if (r == 0) {
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb) {
+            xm[qb] = ws.m_ref[qb];
+            xm[kQB + qb] = ws.l_part[qb];
+          }
+        }
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const f32x16& o = ws.o[2 * r + d2][qb];
+              const f32x4 v = {o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
+              const int slot = (d2 * kQB + qb) * 4 + j;  // 0 .. 15
+              ((RA_LDS f32x4*)(slot < 8 ? xb0 : xb1))[(slot & 7) * 64 + lane] = v;
+            }
+      }
+      __syncthreads();
+      if (grp == 0) {
+        if (r == 0) {
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb) {
+            const float m0 = ws.m_ref[qb], m1 = xm[qb];
+            const float m = fmaxf(m0, m1);
+            a0[qb] = m0 == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m0 - m) * p.sl2);
+            a1[qb] = m1 == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * p.sl2);
+            ws.l_part[qb] = a0[qb] * ws.l_part[qb] + a1[qb] * xm[kQB + qb];
+            ws.m_ref[qb] = m;
+          }
+        }
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int slot = (d2 * kQB + qb) * 4 + j;
+              const f32x4 v = ((RA_LDS f32x4*)(slot < 8 ? xb0 : xb1))[(slot & 7) * 64 + lane];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                ws.o[2 * r + d2][qb][4 * j + e] = a0[qb] * ws.o[2 * r + d2][qb][4 * j + e] + a1[qb] * v[e];
+            }
+      }
+      if (r + 1 < D / 64) __syncthreads();
+    }
+    if (grp == 1) return;
+  }
 
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
@@ -401,10 +600,21 @@ void attn_step_bf16_kernel(StepParams p) {
 
 template <int D>
 hipError_t launch(const StepParams& p, hipStream_t s) {
-  if (p.mask_ext)
-    hipLaunchKernelGGL((attn_step_bf16_kernel<D, true>), dim3(8 * p.per_xcd), dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL((attn_step_bf16_kernel<D, false>), dim3(8 * p.per_xcd), dim3(kThreads), 0, s, p);
+  const dim3 grid(8 * p.per_xcd);
+  if constexpr (D == 128) {
+    if (p.ksplit) {
+      if (p.mask_ext)
+        hipLaunchKernelGGL((attn_step_bf16_ks_kernel<D, true, true>), grid, dim3(2 * kThreads), 0, s, p);
+      else
+        hipLaunchKernelGGL((attn_step_bf16_ks_kernel<D, false, true>), grid, dim3(2 * kThreads), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  if (p.mask_ext) {
+    hipLaunchKernelGGL((attn_step_bf16_kernel<D, true>), grid, dim3(kThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((attn_step_bf16_kernel<D, false>), grid, dim3(kThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 

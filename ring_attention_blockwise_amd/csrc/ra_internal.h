@@ -44,6 +44,7 @@ struct StepParams {
   int per_xcd;              // ceil(n_work / 8)
   int lpt;                  // 1: each XCD's items are whole heads, walked heaviest tile first across them
   int first_heavy;          // 1: the first query tiles see the most keys (walk them first)
+  int ksplit;               // bf16, D = 128: eight-wave workgroups splitting each item's key tiles
 };
 
 // dtype: 0 = f32, 1 = bf16; D in {64, 128}.  The work decomposition of p
