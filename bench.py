@@ -297,6 +297,31 @@ def time_graph(ra, name, rank, reps=20):
             "frac_peak": flops / (res["graph"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def time_config(ra, name, rank, reps=3):
+    """Another workload's ring, eager: rank ``rank``'s forward (all steps,
+    fused merges) on the named configuration."""
+    import torch
+    from seeded_inputs import workload
+    w = workload(name)
+    q, ks, vs, o, lse = build_inputs(ra, w, rank)
+    kw = dict(S=w.S, P=w.P, rank=rank, order=w.order, causal=w.causal, scale=w.scale)
+    ra.ra_rank_forward(q, ks, vs, o, lse, **kw)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        ra.ra_rank_forward(q, ks, vs, o, lse, **kw)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = algorithmic_flops(w, rank)
+    del q, ks, vs, o, lse
+    torch.cuda.empty_cache()
+    return {"kernel": f"rank_forward_{w.S // 1024}k_{'causal' if w.causal else 'noncausal'}", "workload": name,
+            "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "frac_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def time_merge(ra, rows, D, reps=20):
     """Standalone merge, rotating buffer sets so the working set exceeds the
     256 MB Infinity Cache."""
@@ -516,6 +541,7 @@ def main():
             aux.append(time_backward(ra, w, rank, window=4096))
         if w.dtype == "bf16":
             aux.append(time_graph(ra, "bf16_gqa32x8_d128_s32k_ring8_zigzag_causal", 0))
+            aux.append(time_config(ra, "bf16_mha16_b2_d128_s64k_ring8_contiguous_full", 0))
         aux.append(time_merge(ra, w.B * (w.S // w.P) * w.Hq, w.D))
         aux.append(time_relayout(ra, 2, 8192, 16, 128, 8))
         aux.extend(time_ulysses_pieces(ra, 2, 8192, 16, 128, 8))
