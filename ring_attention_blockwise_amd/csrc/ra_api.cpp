@@ -284,26 +284,32 @@ bool build_params(const ra_step_desc* d, const void* q, const void* k, const voi
   }
   for (int i = p->nqs; i < 2; ++i) p->qs_start[i] = p->qs_len[i] = p->qs_off[i] = 0;
   for (int i = p->nks; i < 2; ++i) p->ks_start[i] = p->ks_len[i] = p->ks_off[i] = 0;
-  // bf16, D = 128: when the query tiles that see some key of the block give
-  // fewer than two workgroups per CU, eight-wave workgroups split each item's
-  // key tiles between two wave sets (two waves per SIMD either way).
+  // bf16, D = 128: eight-wave workgroups split each item's key tiles between
+  // two wave sets when the query tiles with work give fewer than two
+  // workgroups per CU, or fewer than four and very unequal ones (the
+  // heaviest, by its first and last rows' visible keys, half again the
+  // average: a diagonal or a window over an earlier block).
   p->ksplit = 0;
   if (d->dtype == RA_DTYPE_BF16 && d->D == 128) {
     const int bq = ra::step_rows(d->dtype);
-    int64_t active = 0;
+    int64_t active = 0, total = 0, heaviest = 0;
     for (int i = 0; i < p->nqs; ++i)
       for (int64_t off = 0; off < p->qs_len[i]; off += bq) {
         const int64_t rows = std::min((int64_t)bq, (int64_t)p->qs_len[i] - off);
-        for (int j = 0; j < p->nks; ++j)
-          if (span_sees(p->qs_start[i] + off, rows, p->ks_start[j], p->ks_len[j], p->causal != 0, m)) {
-            ++active;
-            break;
-          }
+        const int64_t r0 = p->qs_start[i] + off;
+        const int64_t w = visible_keys(*p, m, r0) + visible_keys(*p, m, r0 + rows - 1);
+        if (w == 0) continue;
+        ++active;
+        total += w;
+        heaviest = std::max(heaviest, w);
       }
     int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) ==
-                                                 hipSuccess)
-      p->ksplit = active * d->B * d->Hq < 2 * (int64_t)cus ? 1 : 0;
+    if (active > 0 && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
+      const int64_t items = active * d->B * d->Hq;
+      const bool unequal = 2 * heaviest * active >= 3 * total;
+      p->ksplit = (items < 2 * (int64_t)cus || (items < 4 * (int64_t)cus && unequal)) ? 1 : 0;
+    }
   }
   const int bq = ra::step_rows(d->dtype);
   p->qt_span0 = (int)((p->qs_len[0] + bq - 1) / bq);
