@@ -120,12 +120,21 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(uint32_t total, FastDiv 
 //   SEQ2HEAD: in run ((b s_loc + t) P_u + j)  -> out run ((j B + b) s_loc + t)
 //   HEAD2SEQ: the reverse.
 // Threads walk the OUTPUT in order (coalesced stores); each moves one W-byte
-// unit of a run.
+// unit of a run.  SEQ2HEAD's output is destination-major, so blocks taken in
+// order would, for a long stretch, all read the same P_u-th of every token's
+// row; with `spread` (the grid divided by P_u) block i takes output slot
+// (i mod P_u) spread + i / P_u instead, so the blocks in flight read every
+// part of the rows (measured 12% faster on [2, 8192, 16, 128], P_u = 8).
 template <typename W>
 __global__ __launch_bounds__(256) void relayout_kernel(int dir, uint32_t total, FastDiv upr,
-                                                       FastDiv s_loc, FastDiv pu, FastDiv bdim,
+                                                       FastDiv s_loc, FastDiv pu, FastDiv bdim, uint32_t spread,
                                                        const W* __restrict__ in, W* __restrict__ out) {
-  const uint32_t base = blockIdx.x * (256u * kUpt) + threadIdx.x;
+  uint32_t blk = blockIdx.x;
+  if (spread) {
+    const uint32_t q = fdiv(blk, pu);
+    blk = (blk - q * pu.d) * spread + q;
+  }
+  const uint32_t base = blk * (256u * kUpt) + threadIdx.x;
   W v[kUpt];
 #pragma unroll
   for (int k = 0; k < kUpt; ++k) {
@@ -160,9 +169,10 @@ template <typename W>
 hipError_t launch_relayout_w(int dir, uint32_t total, uint32_t units_per_run, int B,
                              long long s_loc, int P_u, const void* in, void* out, hipStream_t s) {
   const uint32_t blocks = (total + 256u * kUpt - 1) / (256u * kUpt);
+  const uint32_t spread = (dir == 0 && blocks % (uint32_t)P_u == 0) ? blocks / (uint32_t)P_u : 0u;
   hipLaunchKernelGGL(relayout_kernel<W>, dim3(blocks), dim3(256), 0, s, dir, total,
                      make_fastdiv(units_per_run), make_fastdiv((uint32_t)s_loc),
-                     make_fastdiv((uint32_t)P_u), make_fastdiv((uint32_t)B), (const W*)in, (W*)out);
+                     make_fastdiv((uint32_t)P_u), make_fastdiv((uint32_t)B), spread, (const W*)in, (W*)out);
   return hipGetLastError();
 }
 
@@ -175,7 +185,8 @@ hipError_t launch_relayout_w(int dir, uint32_t total, uint32_t units_per_run, in
 // piece j holds run j of every token.  Grouping SEQ: tensor i is
 // [B, P_u, s_loc, run_i] (global token order, block u from source u) and
 // piece u holds block u.  blockIdx.y picks the tensor; threads walk the
-// destination in order (coalesced stores), one W-byte unit each.
+// destination in order (coalesced stores), one W-byte unit each; towards the
+// pieces the blocks are spread over the destinations as in the relayout.
 struct PieceSec {
   const char* src;       // tensor or pieces, by direction
   char* dst;
@@ -189,12 +200,18 @@ struct PieceArgs {
   uint32_t piece;        // units per piece
   FastDiv s_loc, pu, bdim;
   int group, to_pieces;
+  uint32_t spread;       // 0, or gridDim.x / P_u: block i takes slot (i mod P_u) spread + i / P_u
 };
 
 template <typename W>
 __global__ __launch_bounds__(256) void pieces_kernel(PieceArgs a) {
   const PieceSec sc = a.s[blockIdx.y];
-  const uint32_t base = blockIdx.x * (256u * kUpt) + threadIdx.x;
+  uint32_t blk = blockIdx.x;
+  if (a.spread) {
+    const uint32_t q = fdiv(blk, a.pu);
+    blk = (blk - q * a.pu.d) * a.spread + q;
+  }
+  const uint32_t base = blk * (256u * kUpt) + threadIdx.x;
   W v[kUpt];
   long long dsts[kUpt];
 #pragma unroll
@@ -238,7 +255,9 @@ __global__ __launch_bounds__(256) void pieces_kernel(PieceArgs a) {
 template <typename W>
 hipError_t launch_pieces_w(const PieceArgs& a, int n, uint32_t max_total, hipStream_t s) {
   const dim3 grid((max_total + 256u * kUpt - 1) / (256u * kUpt), (unsigned)n);
-  hipLaunchKernelGGL(pieces_kernel<W>, grid, dim3(256), 0, s, a);
+  PieceArgs b = a;
+  b.spread = (a.to_pieces && grid.x % a.pu.d == 0) ? grid.x / a.pu.d : 0u;
+  hipLaunchKernelGGL(pieces_kernel<W>, grid, dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
