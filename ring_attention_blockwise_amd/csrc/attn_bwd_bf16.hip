@@ -463,18 +463,20 @@ struct KvState {
   f32x16 acc[kD / 32];             // dK^T or dV^T accumulators
 };
 
-// Tile t of the list from buffer PAR while tile t+1 is copied into PAR ^ 1;
+// Tile t of the list from buffers CUR while tile t+1 is copied into NXT;
 // te: end of this wave group's part of the list (tiles at or past it only
-// keep the group in step with the other at the barrier).
-template <int PAR, bool kDK, bool kExt>
+// keep the group in step with the other at the barrier).  kPOut (dK only):
+// also leave the tile's P, rounded to bf16, at pout (2 KB per wave).
+template <int CUR, int NXT, bool kDK, bool kExt, bool kPOut = false>
 __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPlan& qp, const KvItem& it,
                                const KvStage& stg, QCursor& cur, int t, int te, RA_LDS char* const* qbuf,
-                               RA_LDS char* const* dbuf, RA_LDS char* const* lbuf, unsigned lane, int wave) {
+                               RA_LDS char* const* dbuf, RA_LDS char* const* lbuf, unsigned lane, int wave,
+                               RA_LDS char* pout = nullptr) {
   const StepParams& p = bp.s;
   const QCursor ci = cur;
   if (t + 1 < te) {
     cur.advance(qp);
-    stg.template issue<kExt>(p, qp, cur, it.g, lane, qbuf[PAR ^ 1], dbuf[PAR ^ 1], lbuf[PAR ^ 1]);
+    stg.template issue<kExt>(p, qp, cur, it.g, lane, qbuf[NXT], dbuf[NXT], lbuf[NXT]);
   }
   // this wave's keys against the tile's rows
   const long long qin = (long long)ci.tile * 32;
@@ -488,10 +490,10 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int u = 0; u < kD / 16; ++u) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(qbuf[PAR], rb ^ (32u * u)));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(qbuf[CUR], rb ^ (32u * u)));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.k[u], s, 0, 0, 0);
       if (kDK) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, lds_load16(dbuf[PAR], rb ^ (32u * u)));
+        const bf16x8 b = __builtin_bit_cast(bf16x8, lds_load16(dbuf[CUR], rb ^ (32u * u)));
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, st.v[u], dp, 0, 0, 0);
       }
     }
@@ -501,7 +503,7 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
     const int key = (int)(lane & 31u);
     // window, packed sequences: row i sees key j iff lo_i <= j <= hi_i, the
     // row's range relative to the tile's first row (staged with the tile)
-    const RA_LDS int* rt = (const RA_LDS int*)(lbuf[PAR] + 512);
+    const RA_LDS int* rt = (const RA_LDS int*)(lbuf[CUR] + 512);
     const int dk = kExt ? (int)max(-(1LL << 30), min(1LL << 30, kwg - qglob)) + key : 0;
     if (!kExt && p.causal && kwg + 31 > qglob) {
       // row i sees key j iff qglob + i >= kwg + j
@@ -509,7 +511,7 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = neg_inf_select(dd + 16 * (r >> 3) + (r & 7), s[r]);
     }
-    const RA_LDS float* lt = (const RA_LDS float*)lbuf[PAR];
+    const RA_LDS float* lt = (const RA_LDS float*)lbuf[CUR];
     unsigned b0, b1;
     tr_bases(lane, b0, b1);
     // one 16-row half at a time: P (and dS) of rows 16hf .. 16hf+15, then the
@@ -535,7 +537,7 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
 #pragma unroll
         for (int e = 0; e < 4; ++e) lo[e] = a0[e], lo[e + 4] = a1[e], hi[e] = c0[e], hi[e + 4] = c1[e];
       }
-      f32x8 x;
+      f32x8 x, xp;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // No guard for rows past the tile's end: their Q, dO, L and delta
@@ -547,13 +549,17 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
         if (kExt) a = (lo[e] <= dk && dk <= hi[e]) ? a : kNegInf;
         const float pr = __builtin_amdgcn_exp2f(a);
         x[e] = kDK ? pr * (dp[8 * hf + e] - tv[e]) : pr;
+        if (kPOut) xp[e] = pr;
       }
+      // P as the dV product takes it (the fused kernel's other wave group)
+      if (kPOut)
+        *(RA_LDS bf16x8*)(pout + (wave * 2 + hf) * 1024 + lane * 16) = __builtin_convertvector(xp, bf16x8);
       const bf16x8 xb = __builtin_convertvector(x, bf16x8);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < kD / 32; ++db) {
         const unsigned o0 = (b0 ^ (64u * db)) + 16u * kRowB * hf, o1 = (b1 ^ (64u * db)) + 16u * kRowB * hf;
-        const bf16x8 a = tr_read(kDK ? qbuf[PAR] : dbuf[PAR], o0, o1);
+        const bf16x8 a = tr_read(kDK ? qbuf[CUR] : dbuf[CUR], o0, o1);
         st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb, st.acc[db], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -581,10 +587,10 @@ __device__ __attribute__((always_inline)) inline void kv_pass(KvState<kDK>& st, 
 
   int i = 0;
   for (; i + 1 < iters; i += 2) {
-    kv_tile<0, kDK, kExt>(st, bp, qp, it, stg, cur, tb + i, te, qbuf, dbuf, lbuf, lane, wave);
-    kv_tile<1, kDK, kExt>(st, bp, qp, it, stg, cur, tb + i + 1, te, qbuf, dbuf, lbuf, lane, wave);
+    kv_tile<0, 1, kDK, kExt>(st, bp, qp, it, stg, cur, tb + i, te, qbuf, dbuf, lbuf, lane, wave);
+    kv_tile<1, 0, kDK, kExt>(st, bp, qp, it, stg, cur, tb + i + 1, te, qbuf, dbuf, lbuf, lane, wave);
   }
-  if (i < iters) kv_tile<0, kDK, kExt>(st, bp, qp, it, stg, cur, tb + i, te, qbuf, dbuf, lbuf, lane, wave);
+  if (i < iters) kv_tile<0, 1, kDK, kExt>(st, bp, qp, it, stg, cur, tb + i, te, qbuf, dbuf, lbuf, lane, wave);
 }
 
 // kSplit = false: four waves (one workgroup) per key tile of 128 keys.
@@ -710,6 +716,155 @@ void attn_bwd_kv_kernel(BwdParams bp) {
     }
 }
 
+// dK and dV in one launch: eight waves per key tile of 128 keys.  Waves 0..3
+// run the dK tile above and also leave each query tile's P (bf16, exactly the
+// operand the dV product takes) in LDS; waves 4..7 add dV^T += dO^T P one
+// query tile behind, from that P and the tile's dO while it is still staged.
+// Three stages of Q, dO, L and P keep tile t+1's copy off tile t-1.  The dV
+// waves recompute neither S nor P: the pair issues 32 products per query
+// tile where the two separate kernels issue 40.  Used when the query tiles
+// are not split between wave groups (every CU gets key tiles).
+template <bool kExt>
+__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_kvf_kernel(BwdParams bp) {
+  const StepParams& p = bp.s;
+  __shared__ __attribute__((aligned(16))) char q0_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char q1_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char q2_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char d0_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char d1_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char d2_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char l0_raw[768];
+  __shared__ __attribute__((aligned(16))) char l1_raw[768];
+  __shared__ __attribute__((aligned(16))) char l2_raw[768];
+  __shared__ __attribute__((aligned(16))) char p0_raw[kTileB];  // 4 waves x 2 halves x 1 KB
+  __shared__ __attribute__((aligned(16))) char p1_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char p2_raw[kTileB];
+  const unsigned lane = threadIdx.x & 63u;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = wv & 3;  // the wave's 32 keys within the tile
+
+  KvItem it;
+  if (!decode_kv(bp, it)) return;
+  const QPlan qp = plan_q(p, it.kglob0, it.kcount);
+  if (qp.n == 0) return;
+  const int n = qp.n;
+  const int key = 32 * wave + (int)(lane & 31u);
+  const long long krow = ((long long)it.b * p.Sk + it.klocal0 + key) * p.Hkv + it.g;
+  const int dsub = 4 * (int)(lane >> 5);
+
+  if (wv < 4) {
+    RA_LDS char* const qbuf[3] = {(RA_LDS char*)q0_raw, (RA_LDS char*)q1_raw, (RA_LDS char*)q2_raw};
+    RA_LDS char* const dbuf[3] = {(RA_LDS char*)d0_raw, (RA_LDS char*)d1_raw, (RA_LDS char*)d2_raw};
+    RA_LDS char* const lbuf[3] = {(RA_LDS char*)l0_raw, (RA_LDS char*)l1_raw, (RA_LDS char*)l2_raw};
+    KvState<true> st;
+    {
+      const bool kok = key < it.kcount;
+      const long long ro = ((long long)it.b * p.Sk * p.Hkv + it.g) * (long long)kRowB +
+                           (it.klocal0 + key) * (long long)(p.Hkv * kRowB);
+      const uint16_t* kr = (const uint16_t*)((const char*)p.k + ro);
+      const uint16_t* vr = (const uint16_t*)((const char*)p.v + ro);
+#pragma unroll
+      for (int u = 0; u < kD / 16; ++u) {
+        st.k[u] = kok ? *(const bf16x8*)(kr + 16 * u + 8 * (lane >> 5)) : bf16x8{};
+        st.v[u] = kok ? *(const bf16x8*)(vr + 16 * u + 8 * (lane >> 5)) : bf16x8{};
+      }
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db) st.acc[db] = f32x16{};
+    }
+    KvStage stg;
+    stg.init(bp, it, wave, lane);
+    QCursor cur;
+    cur.first(qp);
+    stg.template issue<kExt>(p, qp, cur, it.g, lane, qbuf[0], dbuf[0], lbuf[0]);
+    wait_loads();
+    __syncthreads();
+    int t = 0;
+    for (; t + 2 < n; t += 3) {
+      kv_tile<0, 1, true, kExt, true>(st, bp, qp, it, stg, cur, t, n, qbuf, dbuf, lbuf, lane, wave,
+                                      (RA_LDS char*)p0_raw);
+      kv_tile<1, 2, true, kExt, true>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, dbuf, lbuf, lane, wave,
+                                      (RA_LDS char*)p1_raw);
+      kv_tile<2, 0, true, kExt, true>(st, bp, qp, it, stg, cur, t + 2, n, qbuf, dbuf, lbuf, lane, wave,
+                                      (RA_LDS char*)p2_raw);
+    }
+    if (t < n)
+      kv_tile<0, 1, true, kExt, true>(st, bp, qp, it, stg, cur, t, n, qbuf, dbuf, lbuf, lane, wave,
+                                      (RA_LDS char*)p0_raw);
+    if (t + 1 < n)
+      kv_tile<1, 2, true, kExt, true>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, dbuf, lbuf, lane, wave,
+                                      (RA_LDS char*)p1_raw);
+    if (key >= it.kcount) return;
+    float* dst = bp.dk + krow * kD;
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 32 * db + 8 * j + dsub;
+        float4 r = *(const float4*)(dst + c);
+        r.x += st.acc[db][4 * j] * p.scale;
+        r.y += st.acc[db][4 * j + 1] * p.scale;
+        r.z += st.acc[db][4 * j + 2] * p.scale;
+        r.w += st.acc[db][4 * j + 3] * p.scale;
+        *(float4*)(dst + c) = r;
+      }
+    return;
+  }
+
+  // dV waves: query tile t-1 during the dK waves' tile t (stage (t-1) mod 3)
+  f32x16 acc[kD / 32];
+#pragma unroll
+  for (int db = 0; db < kD / 32; ++db) acc[db] = f32x16{};
+  unsigned b0, b1;
+  tr_bases(lane, b0, b1);
+  QCursor cur;  // tile t-1
+  cur.first(qp);
+  const long long kwg = it.kglob0 + 32 * wave;
+  const bool has_keys = 32 * wave < it.kcount;
+  __syncthreads();  // the dK waves' first tile is staged
+  for (int t = 0; t <= n; ++t) {
+    if (t > 0) {
+      // the dK waves wrote P of this tile only where they had work (the same
+      // test as theirs)
+      const long long qin = (long long)cur.tile * 32;
+      const long long qglob = (cur.span ? p.qs_start[1] : p.qs_start[0]) + qin;
+      const int qcount = (int)min(32LL, (cur.span ? p.qs_len[1] : p.qs_len[0]) - qin);
+      const bool live = has_keys && (!p.causal || kwg <= qglob + qcount - 1);
+      const int ix = (t - 1) % 3;
+      RA_LDS char* const dt = ix == 0 ? (RA_LDS char*)d0_raw : ix == 1 ? (RA_LDS char*)d1_raw : (RA_LDS char*)d2_raw;
+      RA_LDS char* const pt = ix == 0 ? (RA_LDS char*)p0_raw : ix == 1 ? (RA_LDS char*)p1_raw : (RA_LDS char*)p2_raw;
+      if (live) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const bf16x8 xb = *(const RA_LDS bf16x8*)(pt + (wave * 2 + hf) * 1024 + lane * 16);
+#pragma unroll
+          for (int db = 0; db < kD / 32; ++db) {
+            const unsigned o0 = (b0 ^ (64u * db)) + 16u * kRowB * hf, o1 = (b1 ^ (64u * db)) + 16u * kRowB * hf;
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(dt, o0, o1), xb, acc[db], 0, 0, 0);
+          }
+        }
+      }
+      cur.advance(qp);
+    }
+    // one barrier per dK tile; none after the last (nothing is staged then)
+    if (t < n) __syncthreads();
+  }
+  if (key >= it.kcount) return;
+  float* dst = bp.dv + krow * kD;
+#pragma unroll
+  for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 32 * db + 8 * j + dsub;
+      float4 r = *(const float4*)(dst + c);
+      r.x += acc[db][4 * j];
+      r.y += acc[db][4 * j + 1];
+      r.z += acc[db][4 * j + 2];
+      r.w += acc[db][4 * j + 3];
+      *(float4*)(dst + c) = r;
+    }
+}
+
 // ===========================================================================
 // delta = rowsum(dO * O): 16 lanes per row of 128, 8 elements per lane.
 template <typename T>
@@ -754,21 +909,19 @@ hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.n_kwork > 0) {
-    const dim3 grid(8 * p.per_xcd_kv);
-    const dim3 blk(p.kv_split ? 2 * kThreads : kThreads);
-    // dV kernel, then dK kernel
+    const dim3 grid(8 * p.per_xcd_kv), blk(2 * kThreads);
+    // split query tiles: the dV kernel, then the dK kernel; otherwise both
+    // in one fused launch
     if (ext && p.kv_split) {
       hipLaunchKernelGGL((attn_bwd_kv_kernel<false, true, true>), grid, blk, 0, s, p);
       hipLaunchKernelGGL((attn_bwd_kv_kernel<true, true, true>), grid, blk, 0, s, p);
     } else if (ext) {
-      hipLaunchKernelGGL((attn_bwd_kv_kernel<false, true, false>), grid, blk, 0, s, p);
-      hipLaunchKernelGGL((attn_bwd_kv_kernel<true, true, false>), grid, blk, 0, s, p);
+      hipLaunchKernelGGL(attn_bwd_kvf_kernel<true>, grid, blk, 0, s, p);
     } else if (p.kv_split) {
       hipLaunchKernelGGL((attn_bwd_kv_kernel<false, false, true>), grid, blk, 0, s, p);
       hipLaunchKernelGGL((attn_bwd_kv_kernel<true, false, true>), grid, blk, 0, s, p);
     } else {
-      hipLaunchKernelGGL((attn_bwd_kv_kernel<false, false, false>), grid, blk, 0, s, p);
-      hipLaunchKernelGGL((attn_bwd_kv_kernel<true, false, false>), grid, blk, 0, s, p);
+      hipLaunchKernelGGL(attn_bwd_kvf_kernel<false>, grid, blk, 0, s, p);
     }
   }
   return hipGetLastError();
