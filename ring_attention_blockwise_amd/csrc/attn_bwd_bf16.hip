@@ -593,7 +593,8 @@ __device__ __attribute__((always_inline)) inline void kv_pass(KvState<kDK>& st, 
   if (i < iters) kv_tile<0, 1, kDK, kExt>(st, bp, qp, it, stg, cur, tb + i, te, qbuf, dbuf, lbuf, lane, wave);
 }
 
-// kSplit = false: four waves (one workgroup) per key tile of 128 keys.
+// kSplit = false: four waves (one workgroup) per key tile of 128 keys (the
+// launcher uses the fused kernel below instead).
 // kSplit = true: eight waves, two groups of four over the same 128 keys; group
 // 0 takes the first half of the query-tile list and group 1 the rest, and
 // group 1 hands its partial sums to group 0 through LDS at the end (a fixed
