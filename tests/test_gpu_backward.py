@@ -62,6 +62,11 @@ SMALL = [
     ("noncausal_b2", 2, 4, 1, 512, 4, "contiguous", False),
     ("ragged_zigzag", 1, 4, 2, 1400, 4, "zigzag", True),
     ("single_rank", 1, 4, 1, 384, 1, "zigzag", True),
+    # more key tiles with work than the GPU has CUs (B x Hkv x active tiles >
+    # 256): the fused dK/dV kernel; rank 1's second step (192 tiles) takes the
+    # split kernels
+    ("fused_dkdv_zigzag_b3", 3, 16, 16, 2048, 2, "zigzag", True),
+    ("fused_dkdv_noncausal_b5", 5, 16, 16, 1024, 2, "contiguous", False),
 ]
 
 
