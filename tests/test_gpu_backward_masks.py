@@ -82,6 +82,9 @@ CASES = [
     ("packed_window_zigzag", 1, 4, 2, 1024, 4, "zigzag", True, 90, [0, 257, 600, 800, 1024]),
     ("ragged_packed_window", 1, 4, 2, 1400, 4, "zigzag", True, 77, [0, 9, 700, 1399, 1400]),
     ("single_rank_packed", 1, 4, 1, 384, 1, "zigzag", True, 0, [0, 200, 384]),
+    # more key tiles with work than the GPU has CUs on each rank's first step:
+    # the fused masked dK/dV kernel (later steps, with few tiles, the split ones)
+    ("fused_window600_packed_b3", 3, 16, 16, 2048, 2, "zigzag", True, 600, [0, 700, 701, 1500, 2048]),
 ]
 
 
