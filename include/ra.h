@@ -300,15 +300,54 @@ typedef struct ra_plan_out {
 
 /*
  * ra_plan -- the index maps and mask classes behind ra_rank_forward, exposed
- * so they can be checked exactly: the source shard of step `step`, both
- * ranks' global spans, the class of each (query span, key span) pair, and the
- * number of FULL / DIAG / SKIP tiles when query rows are cut into tiles of
- * tile_q and key rows into tiles of tile_k (tiles restart at each span; the
- * last tile of a span may be short).  Same requirements on (S, P, rank) as
- * ra_rank_forward, 0 <= step < P, tile sizes >= 1.
+ * so they can be checked exactly: the source shard of step `step` (the static
+ * ring 0 -> 1 -> ... -> P-1 -> 0 of the DeDLOC guide, "The Geo-Distributed
+ * Long-Context Crisis"), both ranks' global spans (ringmaster "Layout":
+ * contiguous shards and the head_tail balancer; "Sequence Parallelism IV ...
+ * Load-Balanced Rings"), the class of each (query span, key span) pair (the
+ * causal skip of the DeDLOC guide, "Best Practices", row "Causal Mask
+ * Handling"), and the number of FULL / DIAG / SKIP tiles when query rows are
+ * cut into tiles of tile_q and key rows into tiles of tile_k (tiles restart
+ * at each span; the last tile of a span may be short).  Same requirements on
+ * (S, P, rank) as ra_rank_forward, 0 <= step < P, tile sizes >= 1.
  */
 int ra_plan(int32_t order, int64_t S, int32_t P, int32_t rank, int32_t step,
             int32_t causal, int32_t tile_q, int32_t tile_k, ra_plan_out* out);
+
+/* Kernels a ring step may launch (reported by ra_rank_launches). */
+#define RA_KERNEL_NONE 0            /* the step launches nothing               */
+#define RA_KERNEL_STEP_F32 1        /* float32 inputs                          */
+#define RA_KERNEL_STEP_BF16 2       /* bf16, four waves, two workgroups per CU */
+#define RA_KERNEL_STEP_BF16_KSPLIT 3/* bf16 D 128, eight waves splitting each
+                                       item's key tiles (few items)            */
+#define RA_KERNEL_STEP_BF16_PIPE 4  /* bf16 D 128, software-pipelined, one
+                                       workgroup per CU                        */
+#define RA_KERNEL_BWD_FUSED 5       /* backward bf16 D 128: dQ, fused dK/dV    */
+#define RA_KERNEL_BWD_SPLIT 6       /* backward bf16 D 128: dQ, dV, dK kernels */
+#define RA_KERNEL_BWD_SIMT 7        /* backward float32 or D 64                */
+
+typedef struct ra_launch_info {
+  int32_t kernel;   /* RA_KERNEL_*                                          */
+  int32_t masked;   /* 1: the window / packed-sequence instantiation        */
+  int32_t items;    /* work items with work: forward, query tiles x heads;
+                       backward, key tiles seen by some query x kv heads    */
+  int32_t grid;     /* workgroups of the (forward or dQ) launch             */
+  int32_t lpt;      /* 1: each XCD walks whole heads, heaviest tile first   */
+  int32_t first_heavy; /* 1: the first query tiles see the most keys        */
+} ra_launch_info;
+
+/*
+ * ra_rank_launches -- which kernels ra_rank_forward(_masked) (backward == 0)
+ * or ra_rank_backward(_masked) (backward == 1) would launch for each of the
+ * P ring steps of `d` under mask `m` (NULL: none), in step order, into
+ * out[0 .. P-1].  Host-only: nothing is enqueued.  The choice depends on the
+ * number of compute units: n_cus > 0 plans for that many; n_cus == 0 uses
+ * the current device's count (which needs a GPU).  The same host code builds
+ * the launches themselves.  Requirements as for the matching call (shapes,
+ * mask); tensor pointers are not needed.
+ */
+int ra_rank_launches(const ra_rank_desc* d, const ra_mask* m, int32_t backward, int32_t n_cus,
+                     ra_launch_info* out);
 
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* ra_last_error(void);

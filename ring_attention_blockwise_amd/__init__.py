@@ -67,6 +67,18 @@ class ra_plan_out(ctypes.Structure):
                 ("tiles_skip", ctypes.c_int64)]
 
 
+class ra_launch_info(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("masked", ctypes.c_int32), ("items", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("lpt", ctypes.c_int32), ("first_heavy", ctypes.c_int32)]
+
+
+RA_KERNEL_NONE, RA_KERNEL_STEP_F32, RA_KERNEL_STEP_BF16, RA_KERNEL_STEP_BF16_KSPLIT = 0, 1, 2, 3
+RA_KERNEL_STEP_BF16_PIPE, RA_KERNEL_BWD_FUSED, RA_KERNEL_BWD_SPLIT, RA_KERNEL_BWD_SIMT = 4, 5, 6, 7
+KERNEL_NAMES = {RA_KERNEL_NONE: "none", RA_KERNEL_STEP_F32: "step_f32", RA_KERNEL_STEP_BF16: "step_bf16",
+                RA_KERNEL_STEP_BF16_KSPLIT: "step_bf16_ksplit", RA_KERNEL_STEP_BF16_PIPE: "step_bf16_pipe",
+                RA_KERNEL_BWD_FUSED: "bwd_fused", RA_KERNEL_BWD_SPLIT: "bwd_split", RA_KERNEL_BWD_SIMT: "bwd_simt"}
+
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python ring_attention_blockwise_amd/build.py`")
 # The library must share PyTorch's HIP runtime: torch hands it device pointers
@@ -94,18 +106,20 @@ lib.ra_ulysses_relayout.argtypes = [_i32, _i32, _i32, _i64, _i32, _i32, _i32, _v
 lib.ra_ulysses_pieces.argtypes = [_i32, _i32, _i32, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_void_p),
                                   ctypes.POINTER(ctypes.c_int64), _vp, _vp]
 lib.ra_plan.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ra_plan_out)]
+lib.ra_rank_launches.argtypes = [ctypes.POINTER(ra_rank_desc), ctypes.POINTER(ra_mask), _i32, _i32,
+                                 ctypes.POINTER(ra_launch_info)]
 lib.ra_last_error.restype = ctypes.c_char_p
 lib.ra_last_error.argtypes = []
 lib.ra_abi_version.restype = ctypes.c_int
 lib.ra_abi_version.argtypes = []
 for _f in ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_rank_forward_masked", "ra_allgather_forward",
            "ra_rank_backward", "ra_rank_backward_masked",
-           "ra_ulysses_relayout", "ra_ulysses_pieces", "ra_plan"):
+           "ra_ulysses_relayout", "ra_ulysses_pieces", "ra_plan", "ra_rank_launches"):
     getattr(lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_rank_forward_masked", "ra_allgather_forward",
            "ra_rank_backward", "ra_rank_backward_masked",
-           "ra_ulysses_relayout", "ra_ulysses_pieces", "ra_plan",
+           "ra_ulysses_relayout", "ra_ulysses_pieces", "ra_plan", "ra_rank_launches",
            "ra_last_error", "ra_abi_version")
 
 
@@ -231,10 +245,12 @@ def ra_rank_forward(q_local, k_shards, v_shards, o, lse, *, S: int, P: int, rank
 
 def ra_rank_forward_masked(q_local, k_shards, v_shards, o, lse, *, S: int, P: int, rank: int, order: str,
                            causal: bool, scale: float | None = None, window: int = 0, cu_seqlens=None,
-                           stream=None) -> None:
+                           cu_seqlens_dev=None, stream=None) -> None:
     """ra_rank_forward with a sliding window (``window`` > 0, causal) and/or
     packed sequences (``cu_seqlens``: boundaries 0 = c_0 < ... < c_n = S, a
-    sequence of ints).  bf16 or float32 inputs."""
+    sequence of ints; ``cu_seqlens_dev``, optional: the same boundaries in a
+    caller-owned int64 GPU tensor, which lets the call be graph-captured).
+    bf16 or float32 inputs."""
     torch = _torch()
     _require(q_local, "q_local", ndim=4)
     _require(k_shards, "k_shards", dtype=q_local.dtype, ndim=5)
@@ -251,24 +267,32 @@ def ra_rank_forward_masked(q_local, k_shards, v_shards, o, lse, *, S: int, P: in
         raise ValueError("o must be [B, S/P, Hq, D] and lse [B, S/P, Hq]")
     d = ra_rank_desc(_dtype_code(q_local), B, Hq, Hkv, D, S, P, rank, ORDERS[order],
                      1 if causal else 0, float(scale if scale is not None else D ** -0.5))
-    m, _keep = _mask(torch, window, cu_seqlens, stream)
+    m, _keep = _mask(torch, window, cu_seqlens, stream, cu_seqlens_dev)
     _check(lib.ra_rank_forward_masked(ctypes.byref(d), ctypes.byref(m), _ptr(q_local), _ptr(k_shards),
                                       _ptr(v_shards), _ptr(o), _ptr(lse), _stream(stream)))
 
 
-def _mask(torch, window, cu_seqlens, stream):
+def _mask(torch, window, cu_seqlens, stream, cu_seqlens_dev=None):
     """An ra_mask and the buffers it points at (keep them alive across the
-    call)."""
+    call).  ``cu_seqlens_dev``: the caller's device copy of the boundaries
+    (int64, contiguous, the same values); without it one is made here with a
+    host-to-device copy, which a captured graph cannot hold."""
     host = dev = None
     n = 0
     if cu_seqlens is not None:
         cu = [int(c) for c in cu_seqlens]
         n = len(cu) - 1
         host = (ctypes.c_int64 * len(cu))(*cu)
-        # allocated on the launch stream, so the stream-ordered allocator keeps
-        # it for the kernels enqueued by the call
-        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
-            dev = torch.tensor(cu, dtype=torch.int64, device="cuda")
+        if cu_seqlens_dev is not None:
+            _require(cu_seqlens_dev, "cu_seqlens_dev", dtype=torch.int64, ndim=1)
+            if cu_seqlens_dev.numel() != len(cu):
+                raise ValueError("cu_seqlens_dev must hold the same boundaries as cu_seqlens")
+            dev = cu_seqlens_dev
+        else:
+            # allocated on the launch stream, so the stream-ordered allocator
+            # keeps it for the kernels enqueued by the call
+            with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+                dev = torch.tensor(cu, dtype=torch.int64, device="cuda")
     m = ra_mask(int(window), n, ctypes.cast(host, ctypes.POINTER(ctypes.c_int64)) if host is not None else None,
                 dev.data_ptr() if dev is not None else None)
     return m, (host, dev)
@@ -316,13 +340,13 @@ def ra_rank_backward(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, d
 
 def ra_rank_backward_masked(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_shards, delta, *,
                             S: int, P: int, rank: int, order: str, causal: bool, scale: float | None = None,
-                            window: int = 0, cu_seqlens=None, stream=None) -> None:
+                            window: int = 0, cu_seqlens=None, cu_seqlens_dev=None, stream=None) -> None:
     """ra_rank_backward under the masks of ra_rank_forward_masked (o, lse
     from that call with the same ``window`` and ``cu_seqlens``)."""
     torch = _torch()
     d = _backward_desc(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_shards, delta,
                        S=S, P=P, rank=rank, order=order, causal=causal, scale=scale)
-    m, _keep = _mask(torch, window, cu_seqlens, stream)
+    m, _keep = _mask(torch, window, cu_seqlens, stream, cu_seqlens_dev)
     _check(lib.ra_rank_backward_masked(ctypes.byref(d), ctypes.byref(m), _ptr(q_local), _ptr(k_shards),
                                        _ptr(v_shards), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk_shards),
                                        _ptr(dv_shards), _ptr(delta), _stream(stream)))
@@ -456,3 +480,30 @@ def ra_plan(order: str, S: int, P: int, rank: int, step: int, causal: bool, tile
 def rank_spans(order: str, S: int, P: int, rank: int):
     """Global spans of ``rank``'s rows, from the library's plan."""
     return ra_plan(order, S, P, rank, 0, True, 1 << 30, 1 << 30)["qspans"]
+
+
+def ra_rank_launches(*, dtype: str, B: int, Hq: int, Hkv: int, D: int, S: int, P: int, rank: int, order: str,
+                     causal: bool, backward: bool = False, n_cus: int = 0, window: int = 0,
+                     cu_seqlens=None) -> list:
+    """Which kernel each ring step of ra_rank_forward (or ra_rank_backward)
+    launches, as a list of P dicts in step order (host-only).  ``n_cus`` = 0
+    asks the current device for its compute units; > 0 plans for that many.
+    ``window`` / ``cu_seqlens`` as for the masked calls (only the host copy
+    of the boundaries is read)."""
+    d = ra_rank_desc(RA_DTYPE_BF16 if dtype == "bf16" else RA_DTYPE_F32, B, Hq, Hkv, D, S, P, rank,
+                     ORDERS[order], 1 if causal else 0, float(D ** -0.5))
+    host = None
+    n = 0
+    if cu_seqlens is not None:
+        cu = [int(c) for c in cu_seqlens]
+        n = len(cu) - 1
+        host = (ctypes.c_int64 * len(cu))(*cu)
+    # the device copy is not read by the plan; the host copy stands in for it
+    # so that the mask passes the same checks as in a real call
+    m = ra_mask(int(window), n, ctypes.cast(host, ctypes.POINTER(ctypes.c_int64)) if host is not None else None,
+                ctypes.cast(host, ctypes.c_void_p).value if host is not None else None)
+    out = (ra_launch_info * P)()
+    _check(lib.ra_rank_launches(ctypes.byref(d), ctypes.byref(m) if (window or n) else None,
+                                1 if backward else 0, int(n_cus), out))
+    return [{"kernel": KERNEL_NAMES[o.kernel], "masked": bool(o.masked), "items": o.items, "grid": o.grid,
+             "lpt": bool(o.lpt), "first_heavy": bool(o.first_heavy)} for o in out]

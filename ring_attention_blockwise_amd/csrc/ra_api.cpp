@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -30,6 +31,22 @@ int ok() {
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Compute units of the current device, queried once per device.  0 if the
+// query fails (no device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 // ---------------------------------------------------------------------------
 // Index maps.  Contiguous: rank r owns [r S/P, (r+1) S/P).  Zigzag: 2P chunks
@@ -156,7 +173,7 @@ int check_mask(const ra_mask* m, int64_t S, bool causal) {
 
 // ---------------------------------------------------------------------------
 int check_step(const ra_step_desc* d, const void* q, const void* k, const void* v, const float* o,
-               const float* lse, uint32_t flags) {
+               const float* lse, uint32_t flags, bool check_ptrs = true) {
   if (!d) return fail(RA_E_INVAL, "descriptor is NULL");
   if (d->dtype != RA_DTYPE_F32 && d->dtype != RA_DTYPE_BF16)
     return fail(RA_E_UNSUPPORTED, "dtype %d not supported (RA_DTYPE_F32 or RA_DTYPE_BF16)", d->dtype);
@@ -182,6 +199,7 @@ int check_step(const ra_step_desc* d, const void* q, const void* k, const void* 
   const int64_t qtiles = (d->qspans[0].len + ra::kBQ - 1) / ra::kBQ +
                          (d->n_qspans > 1 ? (d->qspans[1].len + ra::kBQ - 1) / ra::kBQ : 0);
   if ((int64_t)d->B * d->Hq * qtiles > (int64_t)1 << 30) return fail(RA_E_INVAL, "too many query tiles");
+  if (!check_ptrs) return RA_OK;
   if (d->Sq > 0) {
     if (!q || !o || !lse) return fail(RA_E_INVAL, "q, o and lse must not be NULL");
     if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 4))
@@ -217,7 +235,7 @@ void set_grid(ra::StepParams* p) {
 }
 
 bool build_params(const ra_step_desc* d, const void* q, const void* k, const void* v, float* o,
-                  float* lse, bool accum, ra::StepParams* p, const ra_mask* m = nullptr) {
+                  float* lse, bool accum, int n_cus, ra::StepParams* p, const ra_mask* m = nullptr) {
   if (d->Sq == 0) return false;
   p->q = q;
   p->k = k;
@@ -296,14 +314,13 @@ bool build_params(const ra_step_desc* d, const void* q, const void* k, const voi
         total += w;
         heaviest = std::max(heaviest, w);
       }
-    int dev = 0, cus = 0;
-    if (active > 0 && hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
+    if (active > 0 && n_cus > 0) {
       const int64_t items = active * d->B * d->Hq;
       const bool unequal = 2 * heaviest * active >= 3 * total;
-      p->ksplit = (items < 2 * (int64_t)cus || (items < 4 * (int64_t)cus && unequal)) ? 1 : 0;
+      p->ksplit = (items < 2 * (int64_t)n_cus || (items < 4 * (int64_t)n_cus && unequal)) ? 1 : 0;
     }
   }
+  p->pipe = (d->dtype == RA_DTYPE_BF16 && d->D == 128 && !p->ksplit) ? 1 : 0;
   const int bq = ra::step_rows(d->dtype);
   p->qt_span0 = (int)((p->qs_len[0] + bq - 1) / bq);
   p->n_qtiles = p->qt_span0 + (int)((p->qs_len[1] + bq - 1) / bq);
@@ -315,6 +332,123 @@ bool build_params(const ra_step_desc* d, const void* q, const void* k, const voi
 int launch_step(const ra::StepParams& p, int dtype, int D, void* stream) {
   hipError_t e = ra::launch_attn_step(p, dtype, D, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RA_E_HIP, "attention step launch failed: %s", hipGetErrorString(e));
+  return RA_OK;
+}
+
+// The P steps of one rank's ring (forward or backward): validation once,
+// then the parameters of each step.  The rank drivers launch from these, and
+// ra_rank_launches reports them.
+struct RankRing {
+  const ra_rank_desc* d = nullptr;
+  const ra_mask* m = nullptr;
+  const void *q = nullptr, *k = nullptr, *v = nullptr;
+  float *o = nullptr, *lse = nullptr;
+  int64_t s_loc = 0, shard_elems = 0;
+  size_t esz = 0;
+  ra_step_desc sd;
+
+  // o_ and lse_ are the forward's outputs (the backward passes dq and the
+  // forward's lse, which it only reads: they are checked, never written here)
+  int init(const ra_rank_desc* d_, const ra_mask* m_, const void* q_, const void* k_, const void* v_, float* o_,
+           const float* lse_, bool check_ptrs) {
+    d = d_;
+    m = m_;
+    q = q_;
+    k = k_;
+    v = v_;
+    o = o_;
+    lse = const_cast<float*>(lse_);
+    if (!d) return fail(RA_E_INVAL, "descriptor is NULL");
+    int rc = check_ring(d->order, d->S, d->P, d->rank);
+    if (rc) return rc;
+    rc = check_mask(m, d->S, d->causal != 0);
+    if (rc) return rc;
+    s_loc = d->S / d->P;
+    esz = d->dtype == RA_DTYPE_BF16 ? 2 : 4;
+    sd.dtype = d->dtype;
+    sd.B = d->B;
+    sd.Hq = d->Hq;
+    sd.Hkv = d->Hkv;
+    sd.D = d->D;
+    sd.Sq = s_loc;
+    sd.Sk = s_loc;
+    sd.causal = d->causal;
+    sd.scale = d->scale;
+    const Spans qs = rank_spans(d->order, d->S, d->P, d->rank);
+    sd.n_qspans = qs.n;
+    for (int i = 0; i < 2; ++i) sd.qspans[i] = i < qs.n ? qs.s[i] : ra_span{0, 0};
+    sd.n_kspans = qs.n;
+    for (int i = 0; i < 2; ++i) sd.kspans[i] = sd.qspans[i];
+    shard_elems = (int64_t)d->B * s_loc * d->Hkv * d->D;
+    // every step's descriptor differs from this one only in its key spans
+    return check_step(&sd, q, k, v, o, lse, RA_STEP_INIT, check_ptrs);
+  }
+
+  bool tuned() const { return d->dtype == RA_DTYPE_BF16 && d->D == 128; }
+
+  // Key spans and shard pointers of step s.
+  void at_step(int32_t s, const void** kp, const void** vp, int32_t* src) {
+    *src = ring_src(d->rank, s, d->P);
+    const Spans ks = rank_spans(d->order, d->S, d->P, *src);
+    sd.n_kspans = ks.n;
+    for (int i = 0; i < 2; ++i) sd.kspans[i] = i < ks.n ? ks.s[i] : ra_span{0, 0};
+    *kp = k ? (const char*)k + (size_t)*src * shard_elems * esz : nullptr;
+    *vp = v ? (const char*)v + (size_t)*src * shard_elems * esz : nullptr;
+  }
+
+  // Parameters of forward step s; false when the step launches nothing.
+  bool forward_step(int32_t s, int n_cus, ra::StepParams* p) {
+    if (s_loc == 0) return false;
+    const void *kp, *vp;
+    int32_t src;
+    at_step(s, &kp, &vp, &src);
+    return build_params(&sd, q, kp, vp, o, lse, s > 0, n_cus, p, m);
+  }
+
+  // Parameters of backward step s (o and lse of init() are dq and the
+  // forward's lse); false when the step launches nothing.
+  bool backward_step(int32_t s, int n_cus, const float* fwd_lse, const void* dout, const float* delta, float* dq,
+                     float* dk_shards, float* dv_shards, ra::BwdParams* bp) {
+    if (s_loc == 0) return false;
+    const void *kp, *vp;
+    int32_t src;
+    at_step(s, &kp, &vp, &src);
+    if (!build_params(&sd, q, kp, vp, nullptr, nullptr, s > 0, n_cus, &bp->s, m)) return false;
+    // the dQ kernel's query tiles are kBwdRows rows
+    bp->s.qt_span0 = (int)((bp->s.qs_len[0] + ra::kBwdRows - 1) / ra::kBwdRows);
+    bp->s.n_qtiles = bp->s.qt_span0 + (int)((bp->s.qs_len[1] + ra::kBwdRows - 1) / ra::kBwdRows);
+    bp->s.n_work = bp->s.B * bp->s.Hq * bp->s.n_qtiles;
+    set_grid(&bp->s);
+    bp->dout = dout;
+    bp->lse = fwd_lse;
+    bp->delta = delta;
+    bp->dq = dq;
+    bp->dk = dk_shards ? dk_shards + (size_t)src * shard_elems : nullptr;
+    bp->dv = dv_shards ? dv_shards + (size_t)src * shard_elems : nullptr;
+    // key tiles of kBwdKeys keys over the block's key spans, for the dK/dV kernel
+    bp->kt_span0 = (int)((bp->s.ks_len[0] + ra::kBwdKeys - 1) / ra::kBwdKeys);
+    bp->n_ktiles = bp->kt_span0 + (int)((bp->s.ks_len[1] + ra::kBwdKeys - 1) / ra::kBwdKeys);
+    bp->n_kwork = bp->s.B * bp->s.Hkv * bp->n_ktiles;
+    bp->per_xcd_kv = (bp->n_kwork + 7) / 8;
+    // Two groups of waves share each key tile's query rows (eight-wave
+    // workgroups, separate dV and dK kernels) only when the key tiles with
+    // work would not give every CU a workgroup; otherwise the fused dK/dV
+    // kernel.  Unequal tiles (causal and windowed diagonals) need no split:
+    // each XCD takes one kv head's tiles heaviest first, with work falling
+    // linearly along them, so the tiles dispatched second land on the CUs
+    // whose first tiles were lightest (measured: split 2.74 ms against fused
+    // 2.58 ms for the windowed 131k backward, 30.3 against 30.0 ms causal).
+    bp->kv_split = ((int64_t)bp->s.B * bp->s.Hkv * kv_active(bp->s, m) <= n_cus) ? 1 : 0;
+    return true;
+  }
+};
+
+int check_backward_ptrs(const float* o, const void* dout, const float* dk_shards, const float* dv_shards,
+                        const float* delta) {
+  if (!o || !dout || !dk_shards || !dv_shards || !delta) return fail(RA_E_INVAL, "NULL pointer");
+  if (!aligned(o, 16) || !aligned(dout, 16) || !aligned(dk_shards, 16) || !aligned(dv_shards, 16) ||
+      !aligned(delta, 4))
+    return fail(RA_E_INVAL, "o, dout, dk_shards and dv_shards must be 16-byte aligned, delta 4-byte aligned");
   return RA_OK;
 }
 
@@ -392,7 +526,7 @@ int ra_step(const ra_step_desc* d, const void* q, const void* k, const void* v, 
   int rc = check_step(d, q, k, v, o, lse, flags);
   if (rc) return rc;
   ra::StepParams p;
-  if (!build_params(d, q, k, v, o, lse, flags == RA_STEP_ACCUM, &p)) return ok();
+  if (!build_params(d, q, k, v, o, lse, flags == RA_STEP_ACCUM, device_cus(), &p)) return ok();
   rc = launch_step(p, d->dtype, d->D, stream);
   return rc ? rc : ok();
 }
@@ -404,45 +538,13 @@ int ra_rank_forward(const ra_rank_desc* d, const void* q_local, const void* k_sh
 
 int ra_rank_forward_masked(const ra_rank_desc* d, const ra_mask* m, const void* q_local, const void* k_shards,
                            const void* v_shards, float* o, float* lse, void* stream) {
-  if (!d) return fail(RA_E_INVAL, "descriptor is NULL");
-  int rc = check_ring(d->order, d->S, d->P, d->rank);
+  RankRing ring;
+  int rc = ring.init(d, m, q_local, k_shards, v_shards, o, lse, true);
   if (rc) return rc;
-  rc = check_mask(m, d->S, d->causal != 0);
-  if (rc) return rc;
-  const int64_t s_loc = d->S / d->P;
-  const size_t esz = d->dtype == RA_DTYPE_BF16 ? 2 : 4;
-  // Validate every step's descriptor before the first launch.
-  ra_step_desc sd;
-  sd.dtype = d->dtype;
-  sd.B = d->B;
-  sd.Hq = d->Hq;
-  sd.Hkv = d->Hkv;
-  sd.D = d->D;
-  sd.Sq = s_loc;
-  sd.Sk = s_loc;
-  sd.causal = d->causal;
-  sd.scale = d->scale;
-  const Spans qs = rank_spans(d->order, d->S, d->P, d->rank);
-  sd.n_qspans = qs.n;
-  for (int i = 0; i < 2; ++i) sd.qspans[i] = i < qs.n ? qs.s[i] : ra_span{0, 0};
-  const int64_t shard_elems = (int64_t)d->B * s_loc * d->Hkv * d->D;
-  {
-    const Spans ks = rank_spans(d->order, d->S, d->P, d->rank);
-    sd.n_kspans = ks.n;
-    for (int i = 0; i < 2; ++i) sd.kspans[i] = i < ks.n ? ks.s[i] : ra_span{0, 0};
-    rc = check_step(&sd, q_local, k_shards, v_shards, o, lse, RA_STEP_INIT);
-    if (rc) return rc;
-  }
-  if (s_loc == 0) return ok();
+  const int cus = device_cus();
   for (int32_t s = 0; s < d->P; ++s) {
-    const int32_t src = ring_src(d->rank, s, d->P);
-    const Spans ks = rank_spans(d->order, d->S, d->P, src);
-    sd.n_kspans = ks.n;
-    for (int i = 0; i < 2; ++i) sd.kspans[i] = i < ks.n ? ks.s[i] : ra_span{0, 0};
-    const char* kp = (const char*)k_shards + (size_t)src * shard_elems * esz;
-    const char* vp = (const char*)v_shards + (size_t)src * shard_elems * esz;
     ra::StepParams p;
-    if (!build_params(&sd, q_local, kp, vp, o, lse, s > 0, &p, m)) continue;
+    if (!ring.forward_step(s, cus, &p)) continue;
     rc = launch_step(p, d->dtype, d->D, stream);
     if (rc) return rc;
   }
@@ -473,7 +575,7 @@ int ra_allgather_forward(const ra_rank_desc* d, const void* q_local, const void*
   rc = check_step(&sd, q_local, k_global, v_global, o, lse, RA_STEP_INIT);
   if (rc) return rc;
   ra::StepParams p;
-  if (!build_params(&sd, q_local, k_global, v_global, o, lse, false, &p)) return ok();
+  if (!build_params(&sd, q_local, k_global, v_global, o, lse, false, device_cus(), &p)) return ok();
   rc = launch_step(p, d->dtype, d->D, stream);
   if (rc) return rc;
   return ok();
@@ -489,83 +591,66 @@ int ra_rank_backward(const ra_rank_desc* d, const void* q_local, const void* k_s
 int ra_rank_backward_masked(const ra_rank_desc* d, const ra_mask* m, const void* q_local, const void* k_shards,
                             const void* v_shards, const float* o, const float* lse, const void* dout, float* dq,
                             float* dk_shards, float* dv_shards, float* delta, void* stream) {
-  if (!d) return fail(RA_E_INVAL, "descriptor is NULL");
-  int rc = check_ring(d->order, d->S, d->P, d->rank);
+  RankRing ring;
+  int rc = ring.init(d, m, q_local, k_shards, v_shards, dq, lse, true);
   if (rc) return rc;
-  rc = check_mask(m, d->S, d->causal != 0);
+  if (ring.s_loc == 0) return ok();
+  rc = check_backward_ptrs(o, dout, dk_shards, dv_shards, delta);
   if (rc) return rc;
-  const int64_t s_loc = d->S / d->P;
-  ra_step_desc sd;
-  sd.dtype = d->dtype;
-  sd.B = d->B;
-  sd.Hq = d->Hq;
-  sd.Hkv = d->Hkv;
-  sd.D = d->D;
-  sd.Sq = s_loc;
-  sd.Sk = s_loc;
-  sd.causal = d->causal;
-  sd.scale = d->scale;
-  const Spans qs = rank_spans(d->order, d->S, d->P, d->rank);
-  sd.n_qspans = qs.n;
-  for (int i = 0; i < 2; ++i) sd.qspans[i] = i < qs.n ? qs.s[i] : ra_span{0, 0};
-  sd.n_kspans = qs.n;
-  for (int i = 0; i < 2; ++i) sd.kspans[i] = sd.qspans[i];
-  rc = check_step(&sd, q_local, k_shards, v_shards, dq, lse, RA_STEP_INIT);
-  if (rc) return rc;
-  if (s_loc == 0) return ok();
-  if (!o || !dout || !dk_shards || !dv_shards || !delta) return fail(RA_E_INVAL, "NULL pointer");
-  if (!aligned(o, 16) || !aligned(dout, 16) || !aligned(dk_shards, 16) || !aligned(dv_shards, 16) ||
-      !aligned(delta, 4))
-    return fail(RA_E_INVAL, "o, dout, dk_shards and dv_shards must be 16-byte aligned, delta 4-byte aligned");
-  int dev = 0, n_cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return fail(RA_E_HIP, "cannot query the device's compute units");
-  const int64_t rows = (int64_t)d->B * s_loc * d->Hq;
-  // bf16 with D = 128: the tuned kernels; float32 or D = 64: the SIMT ones
-  const bool tuned = d->dtype == RA_DTYPE_BF16 && d->D == 128;
-  hipError_t e = tuned ? ra::launch_bwd_delta(rows, d->D, 1, dout, o, delta, (hipStream_t)stream)
-                       : ra::launch_simt_delta(rows, d->D, d->dtype, dout, o, delta, (hipStream_t)stream);
+  const int n_cus = device_cus();
+  if (n_cus <= 0) return fail(RA_E_HIP, "cannot query the device's compute units");
+  const int64_t rows = (int64_t)d->B * ring.s_loc * d->Hq;
+  hipError_t e = ring.tuned() ? ra::launch_bwd_delta(rows, d->D, 1, dout, o, delta, (hipStream_t)stream)
+                              : ra::launch_simt_delta(rows, d->D, d->dtype, dout, o, delta, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RA_E_HIP, "delta launch failed: %s", hipGetErrorString(e));
-  const int64_t shard_elems = (int64_t)d->B * s_loc * d->Hkv * d->D;
   for (int32_t s = 0; s < d->P; ++s) {
-    const int32_t src = ring_src(d->rank, s, d->P);
-    const Spans ks = rank_spans(d->order, d->S, d->P, src);
-    sd.n_kspans = ks.n;
-    for (int i = 0; i < 2; ++i) sd.kspans[i] = i < ks.n ? ks.s[i] : ra_span{0, 0};
-    const size_t esz = d->dtype == RA_DTYPE_BF16 ? 2 : 4;
-    const char* kp = (const char*)k_shards + (size_t)src * shard_elems * esz;
-    const char* vp = (const char*)v_shards + (size_t)src * shard_elems * esz;
     ra::BwdParams bp;
-    if (!build_params(&sd, q_local, kp, vp, nullptr, nullptr, s > 0, &bp.s, m)) continue;
-    // the dQ kernel's query tiles are kBwdRows rows
-    bp.s.qt_span0 = (int)((bp.s.qs_len[0] + ra::kBwdRows - 1) / ra::kBwdRows);
-    bp.s.n_qtiles = bp.s.qt_span0 + (int)((bp.s.qs_len[1] + ra::kBwdRows - 1) / ra::kBwdRows);
-    bp.s.n_work = bp.s.B * bp.s.Hq * bp.s.n_qtiles;
-    set_grid(&bp.s);
-    bp.dout = dout;
-    bp.lse = lse;
-    bp.delta = delta;
-    bp.dq = dq;
-    bp.dk = dk_shards + (size_t)src * shard_elems;
-    bp.dv = dv_shards + (size_t)src * shard_elems;
-    // key tiles of kBwdKeys keys over the block's key spans, for the dK/dV kernel
-    bp.kt_span0 = (int)((bp.s.ks_len[0] + ra::kBwdKeys - 1) / ra::kBwdKeys);
-    bp.n_ktiles = bp.kt_span0 + (int)((bp.s.ks_len[1] + ra::kBwdKeys - 1) / ra::kBwdKeys);
-    bp.n_kwork = bp.s.B * bp.s.Hkv * bp.n_ktiles;
-    bp.per_xcd_kv = (bp.n_kwork + 7) / 8;
-    // Two groups of waves share each key tile's query rows (eight-wave
-    // workgroups, separate dV and dK kernels) only when the key tiles with
-    // work would not give every CU a workgroup; otherwise the fused dK/dV
-    // kernel.  Unequal tiles (causal and windowed diagonals) need no split:
-    // each XCD takes one kv head's tiles heaviest first, with work falling
-    // linearly along them, so the tiles dispatched second land on the CUs
-    // whose first tiles were lightest (measured: split 2.74 ms against fused
-    // 2.58 ms for the windowed 131k backward, 30.3 against 30.0 ms causal).
-    bp.kv_split = ((int64_t)bp.s.B * bp.s.Hkv * kv_active(bp.s, m) <= n_cus) ? 1 : 0;
-    e = tuned ? ra::launch_attn_bwd_bf16(bp, (hipStream_t)stream)
-              : ra::launch_attn_bwd_simt(bp, d->dtype, d->D, (hipStream_t)stream);
+    if (!ring.backward_step(s, n_cus, lse, dout, delta, dq, dk_shards, dv_shards, &bp)) continue;
+    e = ring.tuned() ? ra::launch_attn_bwd_bf16(bp, (hipStream_t)stream)
+                     : ra::launch_attn_bwd_simt(bp, d->dtype, d->D, (hipStream_t)stream);
     if (e != hipSuccess) return fail(RA_E_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+int ra_rank_launches(const ra_rank_desc* d, const ra_mask* m, int32_t backward, int32_t n_cus,
+                     ra_launch_info* out) {
+  if (!out) return fail(RA_E_INVAL, "out is NULL");
+  if (backward != 0 && backward != 1) return fail(RA_E_INVAL, "backward must be 0 or 1");
+  if (n_cus < 0) return fail(RA_E_INVAL, "n_cus must be >= 0");
+  RankRing ring;
+  int rc = ring.init(d, m, nullptr, nullptr, nullptr, nullptr, nullptr, false);
+  if (rc) return rc;
+  if (n_cus == 0) {
+    n_cus = device_cus();
+    if (n_cus <= 0) return fail(RA_E_HIP, "cannot query the device's compute units");
+  }
+  for (int32_t s = 0; s < d->P; ++s) {
+    ra_launch_info& li = out[s];
+    li = ra_launch_info{RA_KERNEL_NONE, 0, 0, 0, 0, 0};
+    if (!backward) {
+      ra::StepParams p;
+      if (ring.s_loc == 0 || !ring.forward_step(s, n_cus, &p)) continue;
+      li.kernel = d->dtype == RA_DTYPE_F32 ? RA_KERNEL_STEP_F32
+                  : p.pipe                 ? RA_KERNEL_STEP_BF16_PIPE
+                  : p.ksplit               ? RA_KERNEL_STEP_BF16_KSPLIT
+                                           : RA_KERNEL_STEP_BF16;
+      li.masked = p.mask_ext;
+      li.items = p.n_work;
+      li.grid = 8 * p.per_xcd;
+      li.lpt = p.lpt;
+      li.first_heavy = p.first_heavy;
+    } else {
+      ra::BwdParams bp;
+      if (ring.s_loc == 0 || !ring.backward_step(s, n_cus, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, &bp))
+        continue;
+      li.kernel = !ring.tuned() ? RA_KERNEL_BWD_SIMT : bp.kv_split ? RA_KERNEL_BWD_SPLIT : RA_KERNEL_BWD_FUSED;
+      li.masked = bp.s.mask_ext;
+      li.items = (int32_t)((int64_t)bp.s.B * bp.s.Hkv * kv_active(bp.s, m));
+      li.grid = 8 * bp.s.per_xcd;
+      li.lpt = bp.s.lpt;
+      li.first_heavy = bp.s.first_heavy;
+    }
   }
   return ok();
 }

@@ -124,17 +124,23 @@ class RankCase:
                                  self.causal, self.scale)
 
 
-def sample_rows(S, P, rank, order, n_random, seed):
-    """Local rows at every span boundary plus seeded random rows."""
+def sample_rows(S, P, rank, order, n_random, seed, per_tile=0):
+    """Local rows at every span boundary plus seeded random rows; with
+    ``per_tile`` > 0 also one seeded row inside every run of ``per_tile``
+    consecutive rows of each span (the forward kernel's work items are 256
+    rows of one head, and every head of a sampled row is compared)."""
     spans = im.rank_spans(S, P, rank, order)
     rows = set()
+    rng = np.random.default_rng(seed)
     off = 0
     for _, n in spans:
         for r in (off, off + 1, off + n // 2, off + n - 2, off + n - 1):
             if off <= r < off + n:
                 rows.add(r)
+        if per_tile:
+            for a in range(0, n, per_tile):
+                rows.add(off + a + int(rng.integers(0, min(per_tile, n - a))))
         off += n
-    rng = np.random.default_rng(seed)
     rows.update(int(x) for x in rng.integers(0, S // P, n_random))
     return np.array(sorted(rows), dtype=np.int64)
 

@@ -67,7 +67,15 @@ SMALL = [
     # split kernels
     ("fused_dkdv_zigzag_b3", 3, 16, 16, 2048, 2, "zigzag", True),
     ("fused_dkdv_noncausal_b5", 5, 16, 16, 1024, 2, "contiguous", False),
+    # GQA 32/8 like the 131k workload: the fused kernel's dK waves walk the
+    # four query heads of each key tile's group and the dV waves replay that
+    # walk to take P from LDS; both of rank 0's steps and rank 1's first step
+    # (512 key tiles with work) take it, rank 1's second step the split ones
+    ("fused_dkdv_gqa32x8_b8", 8, 32, 8, 2048, 2, "zigzag", True),
 ]
+
+# which backward kernel must carry some step of rank 0 in the rings above
+FUSED = {"fused_dkdv_zigzag_b3", "fused_dkdv_noncausal_b5", "fused_dkdv_gqa32x8_b8"}
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=[c[0] for c in SMALL])
@@ -78,6 +86,11 @@ def test_small_rings_all_ranks(ra, cfg):
     label, B, Hq, Hkv, S, P, order, causal = cfg
     D = 128
     case = BwdCase(300 + len(label), "bf16", B, Hq, Hkv, D, S, P, order, causal)
+    if label in FUSED:
+        plan = ra.ra_rank_launches(dtype="bf16", B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, P=P, rank=0, order=order,
+                                   causal=causal, backward=True, n_cus=0)
+        say(label, "rank 0 backward kernels", [s_["kernel"] for s_ in plan])
+        assert plan[0]["kernel"] == "bwd_fused"
     s_loc = S // P
     dk = torch.zeros((P, B, s_loc, Hkv, D), device="cuda")
     dv = torch.zeros_like(dk)

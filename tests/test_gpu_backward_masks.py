@@ -85,6 +85,8 @@ CASES = [
     # more key tiles with work than the GPU has CUs on each rank's first step:
     # the fused masked dK/dV kernel (later steps, with few tiles, the split ones)
     ("fused_window600_packed_b3", 3, 16, 16, 2048, 2, "zigzag", True, 600, [0, 700, 701, 1500, 2048]),
+    # GQA 32/8 through the fused masked kernel (step 0 of each rank)
+    ("fused_gqa32x8_window300_b8", 8, 32, 8, 2048, 2, "zigzag", True, 300, None),
 ]
 
 
@@ -97,6 +99,11 @@ def test_small_rings_all_ranks(ra, cfg):
     label, B, Hq, Hkv, S, P, order, causal, window, cu = cfg
     D = 128
     case = MaskedBwdCase(500 + len(label), "bf16", B, Hq, Hkv, D, S, P, order, causal, window=window, cu=cu)
+    if label.startswith("fused"):
+        plan = ra.ra_rank_launches(dtype="bf16", B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, P=P, rank=0, order=order,
+                                   causal=causal, backward=True, n_cus=0, window=window, cu_seqlens=cu)
+        say(label, "rank 0 backward kernels", [(s_["kernel"], s_["masked"]) for s_ in plan])
+        assert plan[0]["kernel"] == "bwd_fused" and plan[0]["masked"]
     s_loc = S // P
     dk = torch.zeros((P, B, s_loc, Hkv, D), device="cuda")
     dv = torch.zeros_like(dk)

@@ -65,6 +65,31 @@ def test_merge_matches_oracle(env, rows, D):
     assert (got_o[a_id & b_id] == 0).all()
 
 
+def test_merge_full_size_every_row(env):
+    """The merge at the size the benchmark times: the 131k rank's 262,144 rows
+    of 128 (8192 local rows x 32 heads), every row against the oracle."""
+    torch, ra = env
+    rows, D = 262144, 128
+    say("ra_lse_merge full size", rows, D)
+    (oa_, la), (ob, lb) = _partials(rows, D, 77)
+    t = lambda x: torch.from_numpy(x).cuda()  # noqa: E731
+    oo = torch.full((rows, D), float("nan"), device="cuda")
+    lo = torch.full((rows,), float("nan"), device="cuda")
+    ra.ra_lse_merge(t(oa_), t(la), t(ob), t(lb), oo, lo)
+    torch.cuda.synchronize()
+    ro, rl = oa.lse_merge(oa_.astype(np.float64), la.astype(np.float64), ob.astype(np.float64),
+                          lb.astype(np.float64))
+    got_o, got_l = oo.cpu().numpy(), lo.cpu().numpy()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    eo, el = float(np.abs(got_o - ro).max()), float(np.abs(got_l[fin] - rl[fin]).max())
+    say(f"max|dO| {eo:.2e} max|dLSE| {el:.2e}")
+    assert eo <= 1e-5 and el <= 1e-5
+    a_id, b_id = np.isneginf(la), np.isneginf(lb)
+    assert np.array_equal(got_o[a_id & ~b_id], ob[a_id & ~b_id])
+    assert np.array_equal(got_o[b_id & ~a_id], oa_[b_id & ~a_id])
+
+
 def test_merge_in_place(env):
     torch, ra = env
     (oa_, la), (ob, lb) = _partials(2048, 128, 3)

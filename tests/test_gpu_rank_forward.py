@@ -73,14 +73,15 @@ FULL = [n for n in WORKLOADS if n != SMALL]
 @pytest.mark.parametrize("which", ["first", "middle", "last"])
 def test_full_size_workloads_sampled(ra, name, which):
     """Full-size workloads in the benchmark's launch configuration; outputs at
-    span boundaries and seeded random rows are compared with the oracle."""
+    span boundaries, one seeded row in every 256-row work item of each span
+    (all heads) and seeded random rows are compared with the oracle."""
     w = workload(name)
     r = {"first": 0, "middle": w.P // 2, "last": w.P - 1}[which]
     say("full size", name, "rank", r)
     case = _case(name)
     o, lse = case.run_rank(ra, r)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
-    rows = sample_rows(w.S, w.P, r, w.order, n_random=8 if w.S > 200000 else 24, seed=r)
+    rows = sample_rows(w.S, w.P, r, w.order, n_random=4 if w.S > 200000 else 8, seed=r, per_tile=256)
     o_ref, l_ref = case.reference(r, rows)
     assert_close(o[:, rows], lse[:, rows], o_ref, l_ref, w.dtype, f"{name} rank {r}")
     if which == "last":

@@ -69,3 +69,70 @@ def test_plan_rejects_bad_rings(args):
         ra.ra_plan(order, S, P, r, s, True, 64, 64)
     assert e.value.status == ra.RA_E_INVAL
     assert ra.ra_last_error()
+
+
+# ---------------------------------------------------------------------------
+# ra_rank_launches: which kernel each step launches (host-only, planned for
+# the 256 compute units of an MI355X)
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_launches_follow_the_pair_classes(name):
+    """A step launches iff some (query span, key span) pair of it is not
+    SKIP in the oracle's classes (step 0 always launches: it writes every
+    row)."""
+    w = WORKLOADS[name]
+    ranks = range(w.P) if w.P <= 8 else (0, w.P // 2, w.P - 1)
+    for r in ranks:
+        for backward in (False, True):
+            plan = ra.ra_rank_launches(dtype=w.dtype, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, S=w.S, P=w.P, rank=r,
+                                       order=w.order, causal=w.causal, backward=backward, n_cus=256)
+            assert len(plan) == w.P
+            for s in range(w.P):
+                classes = im.step_pair_classes(w.S, w.P, r, s, w.order, w.causal)
+                sees = any(c != "SKIP" for row in classes for c in row)
+                assert (plan[s]["kernel"] != "none") == (sees or (s == 0 and not backward)), (r, s, classes)
+
+
+def test_benchmark_workloads_take_the_pipelined_kernel():
+    """The 131k, 64k and 524k rings launch the software-pipelined step
+    kernel on every step, and the fused dK/dV backward; the 32k ring's
+    steps (256 query tiles with work: one per CU) take the key-split
+    kernel."""
+    for name in ("bf16_gqa32x8_d128_s128k_ring16_zigzag_causal", "bf16_mha16_b2_d128_s64k_ring8_contiguous_full",
+                 "bf16_gqa32x8_d128_s512k_ring32_zigzag_causal_khalf"):
+        w = WORKLOADS[name]
+        kw = dict(dtype=w.dtype, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, S=w.S, P=w.P, rank=0, order=w.order,
+                  causal=w.causal, n_cus=256)
+        assert {s["kernel"] for s in ra.ra_rank_launches(**kw)} == {"step_bf16_pipe"}, name
+        assert {s["kernel"] for s in ra.ra_rank_launches(backward=True, **kw)} == {"bwd_fused"}, name
+    w = WORKLOADS["bf16_gqa32x8_d128_s32k_ring8_zigzag_causal"]
+    plan = ra.ra_rank_launches(dtype=w.dtype, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, S=w.S, P=w.P, rank=0,
+                               order=w.order, causal=w.causal, n_cus=256)
+    assert {s["kernel"] for s in plan} == {"step_bf16_ksplit"}
+    w = WORKLOADS["f32_mha2_d64_s512_ring4_contiguous_causal"]
+    plan = ra.ra_rank_launches(dtype=w.dtype, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, S=w.S, P=w.P, rank=3,
+                               order=w.order, causal=w.causal, backward=True, n_cus=256)
+    assert {s["kernel"] for s in plan} == {"bwd_simt"}
+
+
+def test_launches_masked_instantiation():
+    kw = dict(dtype="bf16", B=16, Hq=16, Hkv=4, D=128, S=4096, P=2, rank=0, order="zigzag", causal=True,
+              n_cus=256)
+    plan = ra.ra_rank_launches(window=1500, **kw)
+    assert [(s["kernel"], s["masked"]) for s in plan] == [("step_bf16_pipe", True)] * 2
+    plan = ra.ra_rank_launches(**kw)
+    assert [(s["kernel"], s["masked"]) for s in plan] == [("step_bf16_pipe", False)] * 2
+    # a one-key window cannot reach the held block of step 1 (keys
+    # [1024, 3072), rank 0 holds rows [0, 1024) and [3072, 4096)): no launch
+    plan = ra.ra_rank_launches(window=1, **kw)
+    assert plan[1]["kernel"] == "none"
+
+
+@pytest.mark.parametrize("bad", [dict(n_cus=-1), dict(S=4094), dict(rank=2), dict(window=-3),
+                                 dict(causal=False, window=8), dict(cu_seqlens=[0, 5, 5, 4096])])
+def test_launches_reject_bad_arguments(bad):
+    kw = dict(dtype="bf16", B=1, Hq=8, Hkv=2, D=128, S=4096, P=2, rank=0, order="zigzag", causal=True, n_cus=256)
+    kw.update(bad)
+    with pytest.raises(ra.RaError) as e:
+        ra.ra_rank_launches(**kw)
+    assert e.value.status == ra.RA_E_INVAL
