@@ -8,10 +8,18 @@ algorithmic TFLOP/s: 4*D FLOPs per visible (query, key) pair per head, divided
 by the measured time (pairs hidden by the causal mask are not counted).
 
 Also reported:
-  roofline      the attention step kernel against the bf16 dense MFMA peak,
-                average launch duration from HIP events on the launch stream;
+  ms_per_step_median / _min  of the timed steps (value uses their mean);
+  roofline      the step kernel against the bf16 dense MFMA peak: the same
+                ring's launches issued one by one (the ra_step calls
+                ra_rank_forward makes) with HIP events around each launch on
+                its stream, algorithmic FLOPs over the kernels' own time, and
+                the same against the peak scaled to the GFX clock sampled
+                under load;
+  clock         the GFX clock (amd-smi) while the ring runs back to back;
   cpu_baseline  the CPU oracle (float64 numpy) timed on a sample of rows;
-  aux           HBM rates of the standalone merge and of the relayout.
+  configs       the other workloads' rings (32k, 64k non-causal, 524k);
+  aux           the all-gather form, windowed ring, backward, HIP-graph
+                replay, and HBM rates of the merge and the Ulysses kernels.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 """
@@ -35,8 +43,11 @@ METRIC = "attention TFLOPS per rank-share (1 GPU) and % of bf16 MFMA peak"
 KERNEL_SOURCES = ["ring_attention_blockwise_amd/csrc/attn_step_bf16.hip",
                   "ring_attention_blockwise_amd/csrc/attn_common.h",
                   "ring_attention_blockwise_amd/csrc/ra_internal.h"]
-KERNEL_NAME = "attn_step_bf16_kernel<128, false>"
+KERNEL_NAME = "attn_step_bf16_pipe_kernel<128, false>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_step_traffic.json")
+# the other workloads of the method timed beside the headline (rank 0 each)
+CONFIG_LEGS = ["bf16_gqa32x8_d128_s32k_ring8_zigzag_causal", "bf16_mha16_b2_d128_s64k_ring8_contiguous_full",
+               "bf16_gqa32x8_d128_s512k_ring32_zigzag_causal_khalf"]
 
 
 def kernel_hash() -> str:
@@ -97,6 +108,38 @@ def launches_per_step(ra, w, rank):
     return n
 
 
+def span_pairs(qa, qn, ka, kn, causal):
+    """Visible (query, key) pairs between query positions [qa, qa+qn) and key
+    positions [ka, ka+kn): all of them, or under the causal rule (key <= query)
+    the sum over queries t of the keys of the span at or before t."""
+    if qn <= 0 or kn <= 0:
+        return 0
+    if not causal:
+        return qn * kn
+    total = 0
+    # queries before ka see nothing; from ka + kn - 1 on they see all kn keys
+    t0, t1 = max(qa, ka), qa + qn - 1
+    if t1 < t0:
+        return 0
+    full_from = max(t0, ka + kn - 1)
+    if full_from <= t1:
+        total += (t1 - full_from + 1) * kn
+    lo, hi = t0, min(t1, ka + kn - 2)
+    if hi >= lo:                       # query t sees t - ka + 1 keys
+        n = hi - lo + 1
+        total += n * (lo - ka + 1) + n * (n - 1) // 2
+    return total
+
+
+def step_flops(ra, w, rank, step):
+    """Algorithmic FLOPs of one ring step: 4 D per visible pair per (batch,
+    head), pairs of the rank's query spans against the held shard's key
+    spans."""
+    plan = ra.ra_plan(w.order, w.S, w.P, rank, step, w.causal, 1 << 30, 1 << 30)
+    pairs = sum(span_pairs(a, n, b, m, w.causal) for a, n in plan["qspans"] for b, m in plan["kspans"])
+    return 4.0 * w.D * w.B * w.Hq * pairs, plan
+
+
 def algorithmic_flops(w, rank):
     """4*D per visible pair per (batch, head), pairs from the closed forms of
     the chunk maps (zigzag: c(S+1) per rank; contiguous: s^2 r + s(s+1)/2)."""
@@ -138,6 +181,86 @@ def time_attention(ra, w, rank, steps, warmup):
     del q, ks, vs, o, lse
     torch.cuda.empty_cache()
     return wall, per, ok
+
+
+def time_launches(ra, w, rank, steps):
+    """Per-launch durations of the step kernel on the same ring: each ring
+    step issued as the ra_step call that ra_rank_forward makes for it (INIT
+    at step 0, ACCUM after; steps whose held block is hidden are not
+    launched), with HIP events on the launch stream around every launch,
+    ``steps`` times over.  Returns [(step, flops, [ms per repetition])]."""
+    import torch
+    q, ks, vs, o, lse = build_inputs(ra, w, rank)
+    stream = torch.cuda.current_stream()
+    launches = []
+    for s in range(w.P):
+        flops, plan = step_flops(ra, w, rank, s)
+        if s > 0 and flops == 0:
+            continue
+        launches.append((s, flops, plan))
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
+          for _ in range(steps + 1)]
+    for rep in range(steps + 1):          # repetition 0 warms up
+        for (s, _, plan), (a, b) in zip(launches, ev[rep]):
+            src = plan["src"]
+            a.record(stream)
+            ra.ra_step(q, ks[src], vs[src], o, lse, plan["qspans"], plan["kspans"], causal=w.causal,
+                       scale=w.scale, accum=s > 0, stream=stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    out = [(s, flops, [ev[rep][i][0].elapsed_time(ev[rep][i][1]) for rep in range(1, steps + 1)])
+           for i, (s, flops, _) in enumerate(launches)]
+    del q, ks, vs, o, lse
+    torch.cuda.empty_cache()
+    return out
+
+
+def sample_clock(ra, w, rank, seconds=1.5):
+    """GFX clock (MHz) sampled with amd-smi while the same ring runs back to
+    back for about ``seconds``; None where amd-smi is not available."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception:          # noqa: BLE001 - the clock is a report, not a result
+        return None
+    q, ks, vs, o, lse = build_inputs(ra, w, rank)
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                c = m.get("current_gfxclk")
+                if isinstance(c, (int, float)) and 0 < c < 10000:
+                    samples.append(float(c))
+            except Exception:  # noqa: BLE001
+                pass
+            stop.wait(0.02)
+
+    t = threading.Thread(target=poll)
+    t0 = time.perf_counter()
+    t.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            ra.ra_rank_forward(q, ks, vs, o, lse, S=w.S, P=w.P, rank=rank, order=w.order, causal=w.causal,
+                               scale=w.scale)
+        torch.cuda.synchronize()
+    stop.set()
+    t.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:  # noqa: BLE001
+        pass
+    del q, ks, vs, o, lse
+    torch.cuda.empty_cache()
+    if not samples:
+        return None
+    samples.sort()
+    return {"gfxclk_mhz_median": samples[len(samples) // 2], "gfxclk_mhz_min": samples[0],
+            "gfxclk_mhz_max": samples[-1], "samples": len(samples), "source": "amdsmi current_gfxclk"}
 
 
 def time_allgather(ra, w, rank, ring_ms, reps=5):
@@ -297,9 +420,9 @@ def time_graph(ra, name, rank, reps=20):
             "frac_peak": flops / (res["graph"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def time_config(ra, name, rank, reps=3):
-    """Another workload's ring, eager: rank ``rank``'s forward (all steps,
-    fused merges) on the named configuration."""
+def time_config(ra, name, rank, reps=5):
+    """Another workload's ring: rank ``rank``'s forward (all steps, fused
+    merges), eager, HIP events around each call; mean, median and min."""
     import torch
     from seeded_inputs import workload
     w = workload(name)
@@ -307,19 +430,24 @@ def time_config(ra, name, rank, reps=3):
     kw = dict(S=w.S, P=w.P, rank=rank, order=w.order, causal=w.causal, scale=w.scale)
     ra.ra_rank_forward(q, ks, vs, o, lse, **kw)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
         ra.ra_rank_forward(q, ks, vs, o, lse, **kw)
-    b.record()
+        b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
+    per = [a.elapsed_time(b) for a, b in ev]
+    ms = float(np.mean(per))
     flops = algorithmic_flops(w, rank)
+    kinds = sorted({s["kernel"] for s in ra.ra_rank_launches(dtype=w.dtype, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
+                                                               S=w.S, P=w.P, rank=rank, order=w.order,
+                                                               causal=w.causal)} - {"none"})
     del q, ks, vs, o, lse
     torch.cuda.empty_cache()
     return {"kernel": f"rank_forward_{w.S // 1024}k_{'causal' if w.causal else 'noncausal'}", "workload": name,
-            "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
-            "frac_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+            "rank": rank, "ms": ms, "ms_median": float(np.median(per)), "ms_min": float(min(per)),
+            "TFLOP/s": flops / (ms * 1e-3) / 1e12, "frac_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "step_kernels": kinds}
 
 
 def time_merge(ra, rows, D, reps=20):
@@ -409,6 +537,32 @@ def time_ulysses_pieces(ra, B, s_loc, H, D, P_u, reps=20):
     return res
 
 
+def blas_threads():
+    """Threads numpy's BLAS runs the oracle's products with (the host cores
+    the oracle uses; its element-wise work is single-threaded numpy)."""
+    try:
+        import threadpoolctl
+        n = [i["num_threads"] for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:  # noqa: BLE001
+        pass
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count()
+
+
+def blas_vendor():
+    """numpy's BLAS (name and version) as numpy reports it."""
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg["Build Dependencies"]["blas"]
+        return f"{b.get('name')} {b.get('version')}"
+    except Exception:  # noqa: BLE001 - a report field only
+        return None
+
+
 def cpu_baseline(w, rank, target_s=15.0):
     """The CPU oracle, as it stands, on a bounded sample of rank ``rank``'s rows
     (all heads), scaled to TFLOP/s by the algorithmic FLOPs of those rows."""
@@ -433,11 +587,8 @@ def cpu_baseline(w, rank, target_s=15.0):
         vis = (qsel + 1).sum() if w.causal else qsel.size * w.S
         done_flops += 4.0 * w.D * w.B * w.Hq * float(vis)
         rows_done += rows.size
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
-    return {"value": done_flops / done_s / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": done_flops / done_s / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "blas": blas_vendor(),
             "sample": f"{rows_done} random query rows of rank {rank} x {w.Hq} heads x all visible keys, "
                       f"float64 numpy, {done_s:.1f} s"}
 
@@ -495,7 +646,8 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the 131k zigzag ring)")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-aux", action="store_true", help="skip merge/relayout rates")
+    ap.add_argument("--no-aux", action="store_true", help="skip the other workloads and the aux legs")
+    ap.add_argument("--no-clock", action="store_true", help="skip sampling the GFX clock under load")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (scale reference for HBM byte counters)")
     args = ap.parse_args()
@@ -526,13 +678,25 @@ def main():
     flops = algorithmic_flops(w, rank)
     ms = float(np.mean(per))
     value = flops / (ms * 1e-3) / 1e12
-    nl = launches_per_step(ra, w, rank)
-    launch_us = ms * 1e3 / nl
-    achieved = flops / nl / (launch_us * 1e-6) / 1e12
-    print(f"[bench] attention: {ms:.3f} ms/step (min {min(per):.3f}), {value:.1f} TFLOP/s, "
-          f"{nl} launches of {launch_us:.1f} us", file=sys.stderr, flush=True)
-    aux = []
+    print(f"[bench] attention: {ms:.3f} ms/step (median {np.median(per):.3f}, min {min(per):.3f}), "
+          f"{value:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    # the roofline from the step kernel's own launches: per-launch HIP events
+    lt = time_launches(ra, w, rank, args.steps)
+    kern_ms = [float(np.mean(d)) for _, _, d in lt]
+    kern_flops = sum(f for _, f, _ in lt)
+    achieved = kern_flops / (sum(kern_ms) * 1e-3) / 1e12
+    launch_us = float(np.mean(kern_ms)) * 1e3
+    print(f"[bench] step kernel: {len(lt)} launches, mean {launch_us:.1f} us, {achieved:.1f} TFLOP/s over the "
+          f"kernels' own time", file=sys.stderr, flush=True)
+    clock = None if args.no_clock else sample_clock(ra, w, rank)
+    if clock:
+        print(f"[bench] gfx clock under load: {clock['gfxclk_mhz_median']:.0f} MHz", file=sys.stderr, flush=True)
+    aux, configs = [], []
     if not args.no_aux:
+        for other in CONFIG_LEGS:
+            if other != name and w.dtype == "bf16":
+                print(f"[bench] {other}", file=sys.stderr, flush=True)
+                configs.append(time_config(ra, other, 0))
         aux.append(time_allgather(ra, w, rank, ms))
         if w.dtype == "bf16" and w.causal:
             aux.append(time_window(ra, w, rank, 4096))
@@ -541,11 +705,10 @@ def main():
             aux.append(time_backward(ra, w, rank, window=4096))
         if w.dtype == "bf16":
             aux.append(time_graph(ra, "bf16_gqa32x8_d128_s32k_ring8_zigzag_causal", 0))
-            aux.append(time_config(ra, "bf16_mha16_b2_d128_s64k_ring8_contiguous_full", 0))
         aux.append(time_merge(ra, w.B * (w.S // w.P) * w.Hq, w.D))
         aux.append(time_relayout(ra, 2, 8192, 16, 128, 8))
         aux.extend(time_ulysses_pieces(ra, 2, 8192, 16, 128, 8))
-        for a in aux:
+        for a in configs + aux:
             if "GB/s" in a:
                 print(f"[bench] {a['kernel']}: {a['us']:.1f} us, {a['GB/s']:.0f} GB/s", file=sys.stderr, flush=True)
             else:
@@ -556,6 +719,17 @@ def main():
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, rank)
         cpu["aux"] = cpu_aux_baselines(w, rank)
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(name),
+            "kernel": KERNEL_NAME, "launches_per_step": len(lt), "avg_launch_us": round(launch_us, 2),
+            "launch_us": [round(x * 1e3, 1) for x in kern_ms],
+            "timing": "HIP events around each step-kernel launch on its stream (the ra_step calls "
+                      "ra_rank_forward makes), mean over the timed repetitions"}
+    if clock:
+        peak_at_clk = PEAK_BF16_TFLOPS * clock["gfxclk_mhz_median"] / 2400.0
+        roof["gfxclk_mhz"] = clock["gfxclk_mhz_median"]
+        roof["peak_at_measured_clock"] = round(peak_at_clk, 1)
+        roof["frac_at_measured_clock"] = round(achieved / peak_at_clk, 4)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -564,6 +738,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(float(np.median(per)), 4),
+        "ms_per_step_min": round(float(min(per)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -573,11 +749,10 @@ def main():
                    "ring": w.P, "rank": rank, "order": w.order, "causal": w.causal,
                    "local_query_rows": w.S // w.P},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(name), "kernel": KERNEL_NAME,
-                     "launches_per_step": nl, "avg_launch_us": round(launch_us, 2)},
+        "roofline": roof,
+        "clock": clock,
         "cpu_baseline": cpu,
+        "configs": configs,
         "aux": aux,
         "outputs_finite": ok,
         "wall_s_timed": round(wall, 3),

@@ -16,7 +16,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libra.so")
+# RA_LIBRARY names another build of the same library (the host-sanitizer build
+# the CPU tests run against); by default the in-tree libra.so.
+LIB_PATH = os.environ.get("RA_LIBRARY") or os.path.join(_HERE, "libra.so")
 
 RA_OK, RA_E_INVAL, RA_E_UNSUPPORTED, RA_E_HIP = 0, -1, -2, -3
 RA_DTYPE_F32, RA_DTYPE_BF16 = 0, 1

@@ -67,6 +67,54 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def asan_runtime() -> str | None:
+    """The compiler's shared AddressSanitizer runtime (to preload into the
+    Python process that loads the sanitized build), or None."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    base = os.path.join(rocm, "llvm", "lib", "clang")
+    if not os.path.isdir(base):
+        return None
+    for ver in sorted(os.listdir(base), reverse=True):
+        path = os.path.join(base, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(path):
+            return path
+    return None
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """A second build of the library whose host code of the C ABI (argument
+    checks, index maps, ring and launch plans: ra_api.cpp) is compiled with
+    AddressSanitizer and UndefinedBehaviorSanitizer, linked with the normal
+    kernel objects.  Only host code is instrumented (every sanitizer flag is
+    given to the host compilation alone).  Returns the path of the .so; load
+    it with RA_LIBRARY set to that path and the ASan runtime preloaded."""
+    objs = [os.path.join(BUILD, os.path.splitext(src)[0] + ".o") for src in SOURCES if src != "ra_api.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    out_dir = os.path.join(BUILD, "sanitize")
+    os.makedirs(out_dir, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+    obj = os.path.join(out_dir, "ra_api.o")
+    cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++17", "-fPIC",
+           "-Wall", "-Wno-unused-function", *DEVICE_FLAGS, *san,
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "-c", os.path.join(CSRC, "ra_api.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the sanitized ra_api.cpp:\n{r.stderr}")
+    lib = os.path.join(out_dir, "libra.so")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-mcode-object-version=5", "-shared", "-fPIC",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-shared-libasan", obj, *objs, "-o", lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of the sanitized library failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {lib}")
+    return lib
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

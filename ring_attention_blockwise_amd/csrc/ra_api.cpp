@@ -452,6 +452,28 @@ int check_backward_ptrs(const float* o, const void* dout, const float* dk_shards
   return RA_OK;
 }
 
+// Everything ra_rank_backward enqueues once its arguments are checked:
+// delta = rowsum(dO * O) into `delta`, then per launched step the dQ and
+// dK/dV kernels.
+int run_backward(RankRing& ring, const float* o, const float* lse, const void* dout, float* dq, float* dk_shards,
+                 float* dv_shards, float* delta, void* stream) {
+  const ra_rank_desc* d = ring.d;
+  const int n_cus = device_cus();
+  if (n_cus <= 0) return fail(RA_E_HIP, "cannot query the device's compute units");
+  const int64_t rows = (int64_t)d->B * ring.s_loc * d->Hq;
+  hipError_t e = ring.tuned() ? ra::launch_bwd_delta(rows, d->D, 1, dout, o, delta, (hipStream_t)stream)
+                              : ra::launch_simt_delta(rows, d->D, d->dtype, dout, o, delta, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RA_E_HIP, "delta launch failed: %s", hipGetErrorString(e));
+  for (int32_t s = 0; s < d->P; ++s) {
+    ra::BwdParams bp;
+    if (!ring.backward_step(s, n_cus, lse, dout, delta, dq, dk_shards, dv_shards, &bp)) continue;
+    e = ring.tuned() ? ra::launch_attn_bwd_bf16(bp, (hipStream_t)stream)
+                     : ra::launch_attn_bwd_simt(bp, d->dtype, d->D, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(RA_E_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -597,20 +619,7 @@ int ra_rank_backward_masked(const ra_rank_desc* d, const ra_mask* m, const void*
   if (ring.s_loc == 0) return ok();
   rc = check_backward_ptrs(o, dout, dk_shards, dv_shards, delta);
   if (rc) return rc;
-  const int n_cus = device_cus();
-  if (n_cus <= 0) return fail(RA_E_HIP, "cannot query the device's compute units");
-  const int64_t rows = (int64_t)d->B * ring.s_loc * d->Hq;
-  hipError_t e = ring.tuned() ? ra::launch_bwd_delta(rows, d->D, 1, dout, o, delta, (hipStream_t)stream)
-                              : ra::launch_simt_delta(rows, d->D, d->dtype, dout, o, delta, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(RA_E_HIP, "delta launch failed: %s", hipGetErrorString(e));
-  for (int32_t s = 0; s < d->P; ++s) {
-    ra::BwdParams bp;
-    if (!ring.backward_step(s, n_cus, lse, dout, delta, dq, dk_shards, dv_shards, &bp)) continue;
-    e = ring.tuned() ? ra::launch_attn_bwd_bf16(bp, (hipStream_t)stream)
-                     : ra::launch_attn_bwd_simt(bp, d->dtype, d->D, (hipStream_t)stream);
-    if (e != hipSuccess) return fail(RA_E_HIP, "backward launch failed: %s", hipGetErrorString(e));
-  }
-  return ok();
+  return run_backward(ring, o, lse, dout, dq, dk_shards, dv_shards, delta, stream);
 }
 
 int ra_rank_launches(const ra_rank_desc* d, const ra_mask* m, int32_t backward, int32_t n_cus,
