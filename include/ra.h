@@ -252,6 +252,28 @@ int ra_rank_backward_masked(const ra_rank_desc* d, const ra_mask* m,
                             void* stream);
 
 /*
+ * ra_rank_backward_noalloc -- ra_rank_backward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and results, but the
+ * delta workspace is the library's own scratch array instead of an argument.
+ * The scratch is a file-scope device array of RA_NOALLOC_MAX_ROWS floats
+ * (16 MiB), one per device the library runs on, held until the process ends;
+ * its address is resolved on the first call on each device.  The call itself
+ * allocates nothing.  Requires B * S/P * Hq <= RA_NOALLOC_MAX_ROWS (else
+ * RA_E_INVAL, nothing enqueued), no mask, and everything ra_rank_backward
+ * requires.  The scratch is fully written by each call before it is read, so
+ * nothing carries over between calls; but every call on one device shares
+ * the one array, so calls that overlap on a device (different streams, or
+ * threads without ordering) race and must be ordered by the caller.
+ */
+#define RA_NOALLOC_MAX_ROWS 4194304
+int ra_rank_backward_noalloc(const ra_rank_desc* d, const void* q_local,
+                             const void* k_shards, const void* v_shards,
+                             const float* o, const float* lse, const void* dout,
+                             float* dq, float* dk_shards, float* dv_shards,
+                             void* stream);
+
+/*
  * ra_ulysses_relayout -- the local pack/unpack around the Ulysses all-to-all
  * ("Sequence Parallelism II: DeepSpeed Ulysses and All-to-All Attention": a
  * rank goes from all heads of its tokens to all tokens of a subset of heads).

@@ -104,6 +104,8 @@ lib.ra_rank_backward.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp, _f
                                  _fp, _vp]
 lib.ra_rank_backward_masked.argtypes = [ctypes.POINTER(ra_rank_desc), ctypes.POINTER(ra_mask), _vp, _vp, _vp, _fp,
                                         _fp, _vp, _fp, _fp, _fp, _fp, _vp]
+lib.ra_rank_backward_noalloc.argtypes = [ctypes.POINTER(ra_rank_desc), _vp, _vp, _vp, _fp, _fp, _vp, _fp, _fp, _fp,
+                                         _vp]
 lib.ra_ulysses_relayout.argtypes = [_i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp]
 lib.ra_ulysses_pieces.argtypes = [_i32, _i32, _i32, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_void_p),
                                   ctypes.POINTER(ctypes.c_int64), _vp, _vp]
@@ -115,12 +117,12 @@ lib.ra_last_error.argtypes = []
 lib.ra_abi_version.restype = ctypes.c_int
 lib.ra_abi_version.argtypes = []
 for _f in ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_rank_forward_masked", "ra_allgather_forward",
-           "ra_rank_backward", "ra_rank_backward_masked",
+           "ra_rank_backward", "ra_rank_backward_masked", "ra_rank_backward_noalloc",
            "ra_ulysses_relayout", "ra_ulysses_pieces", "ra_plan", "ra_rank_launches"):
     getattr(lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("ra_step", "ra_lse_merge", "ra_rank_forward", "ra_rank_forward_masked", "ra_allgather_forward",
-           "ra_rank_backward", "ra_rank_backward_masked",
+           "ra_rank_backward", "ra_rank_backward_masked", "ra_rank_backward_noalloc",
            "ra_ulysses_relayout", "ra_ulysses_pieces", "ra_plan", "ra_rank_launches",
            "ra_last_error", "ra_abi_version")
 
@@ -354,6 +356,23 @@ def ra_rank_backward_masked(q_local, k_shards, v_shards, o, lse, dout, dq, dk_sh
                                        _ptr(dv_shards), _ptr(delta), _stream(stream)))
 
 
+RA_NOALLOC_MAX_ROWS = 4194304
+
+
+def ra_rank_backward_noalloc(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_shards, *,
+                             S: int, P: int, rank: int, order: str, causal: bool, scale: float | None = None,
+                             stream=None) -> None:
+    """ra_rank_backward without the delta workspace: the library keeps it in
+    its own device scratch (at most RA_NOALLOC_MAX_ROWS = B * S/P * Hq rows),
+    so the call allocates nothing.  Calls that overlap on one GPU share that
+    scratch and must be ordered by the caller."""
+    d = _backward_desc(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_shards, None,
+                       S=S, P=P, rank=rank, order=order, causal=causal, scale=scale)
+    _check(lib.ra_rank_backward_noalloc(ctypes.byref(d), _ptr(q_local), _ptr(k_shards), _ptr(v_shards), _ptr(o),
+                                        _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk_shards), _ptr(dv_shards),
+                                        _stream(stream)))
+
+
 def _backward_desc(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_shards, delta, *,
                    S, P, rank, order, causal, scale):
     torch = _torch()
@@ -363,7 +382,8 @@ def _backward_desc(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_
     _require(dout, "dout", dtype=q_local.dtype, ndim=4)
     for t, n, nd in ((o, "o", 4), (lse, "lse", 3), (dq, "dq", 4), (dk_shards, "dk_shards", 5),
                      (dv_shards, "dv_shards", 5), (delta, "delta", 3)):
-        _require(t, n, dtype=torch.float32, ndim=nd)
+        if t is not None or n != "delta":
+            _require(t, n, dtype=torch.float32, ndim=nd)
     B, s_loc, Hq, D = q_local.shape
     Hkv = k_shards.shape[3]
     if P * s_loc != S:
@@ -373,7 +393,7 @@ def _backward_desc(q_local, k_shards, v_shards, o, lse, dout, dq, dk_shards, dv_
         raise ValueError("k_shards, v_shards, dk_shards, dv_shards must be [P, B, S/P, Hkv, D]")
     if any(tuple(t.shape) != (B, s_loc, Hq, D) for t in (o, dout, dq)):
         raise ValueError("o, dout and dq must be [B, S/P, Hq, D]")
-    if tuple(lse.shape) != (B, s_loc, Hq) or tuple(delta.shape) != (B, s_loc, Hq):
+    if tuple(lse.shape) != (B, s_loc, Hq) or (delta is not None and tuple(delta.shape) != (B, s_loc, Hq)):
         raise ValueError("lse and delta must be [B, S/P, Hq]")
     return ra_rank_desc(_dtype_code(q_local), B, Hq, Hkv, D, S, P, rank, ORDERS[order],
                         1 if causal else 0, float(scale if scale is not None else D ** -0.5))

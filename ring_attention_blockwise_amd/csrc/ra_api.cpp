@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -474,6 +475,29 @@ int run_backward(RankRing& ring, const float* o, const float* lse, const void* d
   return ok();
 }
 
+// Scratch of ra_rank_backward_noalloc: the backward's delta rows, one copy
+// per device (every device the library runs on holds it until the process
+// ends).  Host code never passes the array's name to a kernel (on the host
+// it is only a stand-in for the symbol): scratch_ptr() resolves its device
+// address once per device, with that device current, and that address is
+// what the launches get.
+constexpr int64_t kScratchRows = RA_NOALLOC_MAX_ROWS;
+__device__ __align__(256) float scratch[kScratchRows];
+
+float* scratch_ptr() {
+  static std::mutex mu;
+  static float* ptrs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptrs[dev] = (float*)p;
+  }
+  return ptrs[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -617,6 +641,24 @@ int ra_rank_backward_masked(const ra_rank_desc* d, const ra_mask* m, const void*
   int rc = ring.init(d, m, q_local, k_shards, v_shards, dq, lse, true);
   if (rc) return rc;
   if (ring.s_loc == 0) return ok();
+  rc = check_backward_ptrs(o, dout, dk_shards, dv_shards, delta);
+  if (rc) return rc;
+  return run_backward(ring, o, lse, dout, dq, dk_shards, dv_shards, delta, stream);
+}
+
+int ra_rank_backward_noalloc(const ra_rank_desc* d, const void* q_local, const void* k_shards,
+                             const void* v_shards, const float* o, const float* lse, const void* dout, float* dq,
+                             float* dk_shards, float* dv_shards, void* stream) {
+  RankRing ring;
+  int rc = ring.init(d, nullptr, q_local, k_shards, v_shards, dq, lse, true);
+  if (rc) return rc;
+  if (ring.s_loc == 0) return ok();
+  const int64_t rows = (int64_t)d->B * ring.s_loc * d->Hq;
+  if (rows > kScratchRows)
+    return fail(RA_E_INVAL, "B * S/P * Hq = %lld rows exceed the %lld rows of the library's scratch",
+                (long long)rows, (long long)kScratchRows);
+  float* delta = scratch_ptr();
+  if (!delta) return fail(RA_E_HIP, "cannot resolve the scratch array's device address");
   rc = check_backward_ptrs(o, dout, dk_shards, dv_shards, delta);
   if (rc) return rc;
   return run_backward(ring, o, lse, dout, dq, dk_shards, dv_shards, delta, stream);

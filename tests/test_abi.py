@@ -151,3 +151,20 @@ def test_masked_entries_reject_bad_masks(window, cu, dev, causal, entry):
                                             FAKE, FAKE, FAKE, FAKE, None)
     assert rc == ra.RA_E_INVAL
     assert ra.ra_last_error()
+
+
+def test_noalloc_backward_rejects_more_rows_than_its_scratch():
+    """ra_rank_backward_noalloc refuses B * S/P * Hq above RA_NOALLOC_MAX_ROWS
+    on the host, before it resolves its scratch or enqueues anything; the
+    descriptor checks of ra_rank_backward come first."""
+    d = ra.ra_rank_desc(1, 1, 16, 1, 128, 1 << 20, 2, 0, 1, 1, 0.088)   # 2^19 rows x 16 heads = 2^23
+    rc = ra.lib.ra_rank_backward_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         None)
+    assert rc == ra.RA_E_INVAL and "scratch" in ra.ra_last_error()
+    assert (1 << 23) > ra.RA_NOALLOC_MAX_ROWS
+    d = ra.ra_rank_desc(1, 1, 16, 1, 128, 4097, 2, 0, 1, 1, 0.088)      # S not divisible by 2P
+    rc = ra.lib.ra_rank_backward_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         None)
+    assert rc == ra.RA_E_INVAL and "divisible" in ra.ra_last_error()
+    m = re.search(r"#define RA_NOALLOC_MAX_ROWS (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == ra.RA_NOALLOC_MAX_ROWS
