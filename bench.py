@@ -43,7 +43,7 @@ METRIC = "attention TFLOPS per rank-share (1 GPU) and % of bf16 MFMA peak"
 KERNEL_SOURCES = ["ring_attention_blockwise_amd/csrc/attn_step_bf16.hip",
                   "ring_attention_blockwise_amd/csrc/attn_common.h",
                   "ring_attention_blockwise_amd/csrc/ra_internal.h"]
-KERNEL_NAME = "attn_step_bf16_pipe_kernel<128, false>"
+KERNEL_NAME = "attn_step_bf16_kernel<128, false>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_step_traffic.json")
 # the other workloads of the method timed beside the headline (rank 0 each)
 CONFIG_LEGS = ["bf16_gqa32x8_d128_s32k_ring8_zigzag_causal", "bf16_mha16_b2_d128_s64k_ring8_contiguous_full",

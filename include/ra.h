@@ -342,11 +342,9 @@ int ra_plan(int32_t order, int64_t S, int32_t P, int32_t rank, int32_t step,
 #define RA_KERNEL_STEP_BF16 2       /* bf16, four waves, two workgroups per CU */
 #define RA_KERNEL_STEP_BF16_KSPLIT 3/* bf16 D 128, eight waves splitting each
                                        item's key tiles (few items)            */
-#define RA_KERNEL_STEP_BF16_PIPE 4  /* bf16 D 128, software-pipelined, one
-                                       workgroup per CU                        */
-#define RA_KERNEL_BWD_FUSED 5       /* backward bf16 D 128: dQ, fused dK/dV    */
-#define RA_KERNEL_BWD_SPLIT 6       /* backward bf16 D 128: dQ, dV, dK kernels */
-#define RA_KERNEL_BWD_SIMT 7        /* backward float32 or D 64                */
+#define RA_KERNEL_BWD_FUSED 4       /* backward bf16 D 128: dQ, fused dK/dV    */
+#define RA_KERNEL_BWD_SPLIT 5       /* backward bf16 D 128: dQ, dV, dK kernels */
+#define RA_KERNEL_BWD_SIMT 6        /* backward float32 or D 64                */
 
 typedef struct ra_launch_info {
   int32_t kernel;   /* RA_KERNEL_*                                          */

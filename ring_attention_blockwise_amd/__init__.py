@@ -75,9 +75,9 @@ class ra_launch_info(ctypes.Structure):
 
 
 RA_KERNEL_NONE, RA_KERNEL_STEP_F32, RA_KERNEL_STEP_BF16, RA_KERNEL_STEP_BF16_KSPLIT = 0, 1, 2, 3
-RA_KERNEL_STEP_BF16_PIPE, RA_KERNEL_BWD_FUSED, RA_KERNEL_BWD_SPLIT, RA_KERNEL_BWD_SIMT = 4, 5, 6, 7
+RA_KERNEL_BWD_FUSED, RA_KERNEL_BWD_SPLIT, RA_KERNEL_BWD_SIMT = 4, 5, 6
 KERNEL_NAMES = {RA_KERNEL_NONE: "none", RA_KERNEL_STEP_F32: "step_f32", RA_KERNEL_STEP_BF16: "step_bf16",
-                RA_KERNEL_STEP_BF16_KSPLIT: "step_bf16_ksplit", RA_KERNEL_STEP_BF16_PIPE: "step_bf16_pipe",
+                RA_KERNEL_STEP_BF16_KSPLIT: "step_bf16_ksplit",
                 RA_KERNEL_BWD_FUSED: "bwd_fused", RA_KERNEL_BWD_SPLIT: "bwd_split", RA_KERNEL_BWD_SIMT: "bwd_simt"}
 
 

@@ -24,13 +24,8 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are turned off for all device code.  Code
 # object v5 loads under every ROCm 7 runtime, including the one bundled with
-# PyTorch, which is the runtime this library shares at run time.  MFMAs keep
-# their accumulators in ordinary vector registers: kernels that run one wave
-# per SIMD (512 registers) would otherwise get every MFMA in the
-# accumulation-register form and copy each score tile out before the
-# softmax; the accumulation registers then hold read-only MFMA operands.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mcode-object-version=5",
-                "-mllvm", "-amdgpu-mfma-vgpr-form"]
+# PyTorch, which is the runtime this library shares at run time.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mcode-object-version=5"]
 
 
 def hipcc() -> str:

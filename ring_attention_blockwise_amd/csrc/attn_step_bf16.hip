@@ -155,20 +155,6 @@ struct Stager {
     }
   }
 
-  // Starts the copy of only the K (or only the V) rows of the tile at cursor
-  // c into dst; rows past `count` load as 0.
-  template <bool kV>
-  __device__ void issue_one(const TileCursor& c, RA_LDS char* dst) const {
-    const long long off = c.local0 * (long long)row_bytes;
-    const int nrec = (c.count() - 1) * (int)row_bytes + 2 * D;
-    const auto r = __builtin_amdgcn_make_buffer_rsrc((void*)((kV ? vhead : khead) + off), (short)0, nrec, kRsrcWord3);
-#pragma unroll
-    for (int i = 0; i < Ly::kDma; ++i) {
-      RA_LDS char* d = dst + (wave * Ly::kDma + i) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (RA_LDS void*)d, 16, (int)(kV ? vo[i] : ko[i]), 0, 0, 0);
-    }
-  }
-
   // Starts the copy of the tile at cursor c into kdst / vdst.  Rows past
   // `count` load as 0: masked keys for K, zero-weighted values for V.
   __device__ void issue(const TileCursor& c, RA_LDS char* kdst, RA_LDS char* vdst) const {
@@ -612,371 +598,10 @@ void attn_step_bf16_ks_kernel(StepParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Software-pipelined variant: one workgroup of four waves per CU, one wave per
-// SIMD with the whole register file (up to 512 registers, the O accumulators
-// in the accumulation registers).  Tile t's softmax runs while the same wave
-// issues tile t-1's P.V products: the matrix core takes those MFMAs while the
-// vector ALU works through the exponentials, which no longer waits for a
-// second wave to overlap them.
-//
-// Iteration t (PAR = t mod 2):
-//   * start the copies of K(t+1) into kbuf[PAR^1] and of V(t) into vbuf[PAR]
-//     (V lags K by one tile: V(t) is used in iteration t+1);
-//   * S(t) = K(t) Q^T from kbuf[PAR];
-//   * the mask of tile t (only tiles on a diagonal or cut short);
-//   * softmax of S(t) (running maximum, exponentials, row sums, bf16 P(t))
-//     interleaved with O += V(t-1) P(t-1) from vbuf[PAR^1];
-//   * the rare rescale of O when a row's reference maximum moved (after the
-//     products of tile t-1, which are relative to the old reference);
-//   * wait for the copies, barrier.
-// After the last tile, O += V(n-1) P(n-1).
-template <int D>
-struct PipeLane {
-  unsigned kb0, vb0;  // K operand read of unit 0, transposing V read of block 0
-};
-
-// O^T += V^T P^T for one tile's probabilities pp from the V tile at vt.
-template <int D>
-__device__ inline void pv_products(WaveState<D>& ws, const bf16x8 (&pp)[kQB][2], const RA_LDS char* vt, unsigned vb0) {
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const unsigned off = (vb0 ^ (64u * db)) + 16 * hf * Layout<D>::kVStride;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vt + off));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vt + off + 4 * Layout<D>::kVStride));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
-        ws.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[qb][hf], ws.o[db][qb], 0, 0, 0);
-    }
-}
-
-// Carried from one iteration to the next: the previous tile's P (bf16) and
-// the factor that moves O from the reference before that tile to the
-// reference after it (applied, when some row moved, before that tile's
-// products are added).
-struct PipeCarry {
-  bf16x8 pp[kQB][2];
-  float alpha[kQB];
-  bool any;
-};
-
-// Softmax of one tile's 32-row query blocks, in pieces that the products of
-// the previous tile are spread over.  Piece 0: the row's maximum over this
-// lane's 16 scores; 1: across the two lane halves, the new reference and the
-// factor that moves O and l to it; 2-5: four exponentials each, summed; 6:
-// the probabilities rounded to bf16, the row sum updated.
-struct SmState {
-  float tmax[kQB], mb[kQB], acc[kQB], alpha[kQB];
-  bool grow[kQB];
-};
-
-template <int D, int QB, int PIECE>
-__device__ inline void sm_piece(f32x16 (&s)[kQB], SmState& sm, WaveState<D>& ws, bf16x8 (&pn)[kQB][2],
-                                const StepParams& p) {
-  if constexpr (PIECE == 0) {
-    float t = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) t = fmaxf(t, s[QB][r]);
-    sm.tmax[QB] = t;
-    asm volatile("" : "+v"(sm.tmax[QB]));
-  } else if constexpr (PIECE == 1) {
-    const float tmax = max_halves(sm.tmax[QB]);
-    const float m_old = ws.m_ref[QB];
-    const float m_new = fmaxf(m_old, tmax);
-    // -inf reference: the difference is +inf and the maximum is taken;
-    // both -inf: NaN compares false and nothing moves
-    const bool grow = (m_new - m_old) * p.sl2 > kTau;
-    sm.grow[QB] = grow;
-    ws.m_ref[QB] = grow ? m_new : m_old;
-    sm.alpha[QB] = grow ? __builtin_amdgcn_exp2f((m_old - m_new) * p.sl2) : 1.f;
-    sm.mb[QB] = ws.m_ref[QB] == kNegInf ? 0.f : ws.m_ref[QB] * p.sl2;
-    asm volatile("" : "+v"(sm.mb[QB]), "+v"(sm.alpha[QB]), "+v"(ws.m_ref[QB]));
-  } else if constexpr (PIECE >= 2 && PIECE <= 5) {
-    constexpr int e0 = 4 * (PIECE - 2);
-    float a = 0.f;
-#pragma unroll
-    for (int e = e0; e < e0 + 4; ++e) {
-      s[QB][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[QB][e], p.sl2, -sm.mb[QB]));
-      a = e == e0 ? s[QB][e] : a + s[QB][e];
-    }
-    sm.acc[QB] = PIECE == 2 ? a : sm.acc[QB] + a;
-    asm volatile("" : "+v"(sm.acc[QB]));
-    asm volatile("" : "+v"(s[QB][e0]), "+v"(s[QB][e0 + 1]), "+v"(s[QB][e0 + 2]), "+v"(s[QB][e0 + 3]));
-  } else {
-    f32x8 lo, hi;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lo[e] = s[QB][e];
-      hi[e] = s[QB][8 + e];
-    }
-    pn[QB][0] = __builtin_convertvector(lo, bf16x8);
-    pn[QB][1] = __builtin_convertvector(hi, bf16x8);
-    ws.l_part[QB] = ws.l_part[QB] * sm.alpha[QB] + sm.acc[QB];
-    asm volatile("" : "+v"(pn[QB][0]), "+v"(pn[QB][1]), "+v"(ws.l_part[QB]));
-  }
-}
-
-template <int D>
-__device__ inline void sm_pieces_all(f32x16 (&s)[kQB], SmState& sm, WaveState<D>& ws, bf16x8 (&pn)[kQB][2],
-                                     const StepParams& p) {
-  sm_piece<D, 0, 0>(s, sm, ws, pn, p);
-  sm_piece<D, 1, 0>(s, sm, ws, pn, p);
-  sm_piece<D, 0, 1>(s, sm, ws, pn, p);
-  sm_piece<D, 1, 1>(s, sm, ws, pn, p);
-  sm_piece<D, 0, 2>(s, sm, ws, pn, p);
-  sm_piece<D, 1, 2>(s, sm, ws, pn, p);
-  sm_piece<D, 0, 3>(s, sm, ws, pn, p);
-  sm_piece<D, 1, 3>(s, sm, ws, pn, p);
-  sm_piece<D, 0, 4>(s, sm, ws, pn, p);
-  sm_piece<D, 1, 4>(s, sm, ws, pn, p);
-  sm_piece<D, 0, 5>(s, sm, ws, pn, p);
-  sm_piece<D, 1, 5>(s, sm, ws, pn, p);
-  sm_piece<D, 0, 6>(s, sm, ws, pn, p);
-  sm_piece<D, 1, 6>(s, sm, ws, pn, p);
-}
-
-// V operand k (= 4 hf + db: keys 16 hf .. +15, columns 32 db .. +31) of the
-// P.V product, by two transposing reads.
-template <int D>
-__device__ inline void vop_load(bf16x8 (&vop)[2 * (D / 32)], int k, const RA_LDS char* vt, unsigned vb0) {
-  const int hf = k / (D / 32), db = k % (D / 32);
-  const unsigned off = (vb0 ^ (64u * db)) + 16 * hf * Layout<D>::kVStride;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vt + off));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vt + off + 4 * Layout<D>::kVStride));
-  vop[k] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Chunk C of the pipelined slot: the product of V operand C/2 with query
-// block C%2's previous probabilities, the operand loads two products ahead,
-// and softmax piece C/2 of query block C%2 (none in the last two chunks).
-// The product is written as one instruction so that it stays in its chunk
-// (the builtin floats freely through the schedule); it accumulates in place
-// into an accumulator no other instruction touches in this slot.
-template <int D, int C>
-__device__ inline void pv_chunk(WaveState<D>& ws, const PipeCarry& pc, bf16x8 (&vop)[2 * (D / 32)], f32x16 (&s)[kQB],
-                                SmState& sm, bf16x8 (&pn)[kQB][2], const StepParams& p, const RA_LDS char* vt,
-                                unsigned vb0) {
-  constexpr int k = C / 2, qb = C % 2, hf = k / (D / 32), db = k % (D / 32);
-  if constexpr (qb == 0 && k + 2 < 2 * (D / 32)) vop_load<D>(vop, k + 2, vt, vb0);
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(ws.o[db][qb]) : "v"(vop[k]), "v"(pc.pp[qb][hf]));
-  if constexpr (C < 14) sm_piece<D, C % 2, C / 2>(s, sm, ws, pn, p);
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-template <int D, int PAR, bool kExt, bool kFirst>
-__device__ inline void pipe_tile(WaveState<D>& ws, PipeCarry& pc, const StepParams& p, const TilePlan& tp,
-                                 const WorkItem& wi, const Stager<D>& st, TileCursor& cur, int t,
-                                 const PipeLane<D>& pl, RA_LDS char* const* kbuf, RA_LDS char* const* vbuf,
-                                 const RA_LDS int* row_lo, const RA_LDS int* row_hi, int lane, int wave) {
-  const TileCursor ti = cur;
-  if (t + 1 < tp.n) {
-    cur.advance(tp);
-    st.template issue_one<false>(cur, kbuf[PAR ^ 1]);
-  }
-  st.template issue_one<true>(ti, vbuf[PAR]);
-
-  // S^T = K Q^T
-  f32x16 s[kQB];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) s[qb] = f32x16{};
-#pragma unroll
-  for (int u = 0; u < D / 16; ++u) {
-    const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(kbuf[PAR], pl.kb0 ^ (32u * u)));
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.q[qb][u], s[qb], 0, 0, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-  for (int u = 2; u < D / 16; ++u) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-  __builtin_amdgcn_sched_barrier(0);
-
-  const int L = lane >> 5;
-  if (ti.masked()) {
-    // see step_tile: key k of the tile is visible to row q iff it lies in the
-    // row's range; the sign bit of the distances selects -inf
-    const long long d0 = wi.qglob0 - ti.glob0 + 1;
-    const int dc = p.causal ? (int)max(-1024LL, min(1024LL, d0)) : 1024;
-    const int base = kExt ? (int)max(-(1LL << 30), min(1LL << 30, ti.glob0 - wi.qglob0)) : 0;
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const int ri = 64 * wave + 32 * qb + (lane & 31);
-      int lim = min(ti.count(), max(0, dc + ri));
-      if (kExt) lim = max(0, min(ti.count(), row_hi[ri] + 1 - base));
-      const int lim_l = lim - 8 * L - 1;
-      const int lo_l = kExt ? 8 * L - max(-1, min(33, row_lo[ri] - base)) : 0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int d = lim_l - (16 * (r >> 3) + (r & 7));
-        if (kExt) d |= lo_l + (16 * (r >> 3) + (r & 7));
-        asm volatile("" : "+v"(d));
-        const unsigned m = (unsigned)(d >> 31);
-        s[qb][r] = __uint_as_float((m & 0xff800000u) | (~m & __float_as_uint(s[qb][r])));
-      }
-    }
-  }
-  // tile t-2 moved some row's reference: bring O (which holds the products
-  // up to tile t-2) to the reference tile t-1's P is relative to
-  if (!kFirst && pc.any) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) ws.o[db][qb] *= pc.alpha[qb];
-    // the products below are single instructions the compiler does not see
-    // as MFMAs: leave the vector writes of O their wait states by hand
-    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // softmax of tile t, interleaved with the products of tile t-1: sixteen
-  // chunks, each one product and a piece of one query block's softmax
-  SmState sm;
-  bf16x8 pn[kQB][2];
-  if (kFirst) {
-    sm_pieces_all<D>(s, sm, ws, pn, p);
-  } else {
-    bf16x8 vop[2 * (D / 32)];
-    vop_load<D>(vop, 0, vbuf[PAR ^ 1], pl.vb0);
-    vop_load<D>(vop, 1, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 0>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 1>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 2>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 3>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 4>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 5>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 6>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 7>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 8>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 9>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 10>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 11>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 12>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 13>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 14>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-    pv_chunk<D, 15>(ws, pc, vop, s, sm, pn, p, vbuf[PAR ^ 1], pl.vb0);
-  }
-  bool anyg = false;
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    anyg |= sm.grow[qb];
-    pc.alpha[qb] = sm.alpha[qb];
-  }
-  pc.any = __builtin_amdgcn_ballot_w64(anyg) != 0;
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) pc.pp[qb][hf] = pn[qb][hf];
-
-  wait_loads();
-  __syncthreads();
-}
-
-template <int D, bool kExt>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_step_bf16_pipe_kernel(StepParams p) {
-  typedef Layout<D> Ly;
-  __shared__ __attribute__((aligned(16))) char k0_raw[Ly::kKTileBytes];
-  __shared__ __attribute__((aligned(16))) char k1_raw[Ly::kKTileBytes];
-  __shared__ __attribute__((aligned(16))) char v0_raw[Ly::kVTileBytes];
-  __shared__ __attribute__((aligned(16))) char v1_raw[Ly::kVTileBytes];
-  RA_LDS char* const kbuf[2] = {(RA_LDS char*)k0_raw, (RA_LDS char*)k1_raw};
-  RA_LDS char* const vbuf[2] = {(RA_LDS char*)v0_raw, (RA_LDS char*)v1_raw};
-  __shared__ int lo_raw[kBQBf16], hi_raw[kBQBf16];
-  const RA_LDS int* row_lo = (const RA_LDS int*)lo_raw;
-  const RA_LDS int* row_hi = (const RA_LDS int*)hi_raw;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  WorkItem wi;
-  if (!decode_work<kBQBf16>(p, wi)) return;
-  const TilePlan tp = plan_tiles(p, wi.qglob0, wi.qglob0 + wi.qrows - 1);
-  if (tp.n == 0) {
-    store_identity<D, kThreads>(p, wi);
-    return;
-  }
-  if (kExt) {
-    for (int r = threadIdx.x; r < kBQBf16; r += kThreads) {
-      const long long t = wi.qglob0 + r;
-      lo_raw[r] = (int)max(-(1LL << 30), min(1LL << 30, key_lo(p, t) - wi.qglob0));
-      hi_raw[r] = (int)max(-(1LL << 30), min(1LL << 30, key_hi(p, t) - wi.qglob0));
-    }
-  }
-
-  const Lane<D> ln((unsigned)(p.Hkv * D * 2), wave);
-  Stager<D> st;
-  st.init(p, wi, ln);
-  TileCursor cur;
-  cur.first(tp);
-  st.template issue_one<false>(cur, kbuf[0]);
-  PipeLane<D> pl;
-  pl.kb0 = ln.kb0();
-  pl.vb0 = ln.vb0();
-  WaveState<D> ws;
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int wrow = 64 * wave + 32 * qb + (lane & 31);
-    const long long orow = ((long long)wi.b * p.Sq + wi.qlocal0 + wrow) * p.Hq + wi.h;
-    const uint16_t* qrow = (const uint16_t*)p.q + orow * D;
-#pragma unroll
-    for (int u = 0; u < D / 16; ++u)
-      ws.q[qb][u] = wrow < wi.qrows ? *(const bf16x8*)(qrow + 16 * u + 8 * (lane >> 5)) : bf16x8{};
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) ws.o[db][qb] = f32x16{};
-    ws.m_ref[qb] = kNegInf;
-    ws.l_part[qb] = 0.f;
-  }
-  PipeCarry pc;
-  wait_loads();
-  __syncthreads();
-
-  pipe_tile<D, 0, kExt, true>(ws, pc, p, tp, wi, st, cur, 0, pl, kbuf, vbuf, row_lo, row_hi, lane, wave);
-  int t = 1;
-  for (; t + 1 < tp.n; t += 2) {
-    pipe_tile<D, 1, kExt, false>(ws, pc, p, tp, wi, st, cur, t, pl, kbuf, vbuf, row_lo, row_hi, lane, wave);
-    pipe_tile<D, 0, kExt, false>(ws, pc, p, tp, wi, st, cur, t + 1, pl, kbuf, vbuf, row_lo, row_hi, lane, wave);
-  }
-  if (t < tp.n) pipe_tile<D, 1, kExt, false>(ws, pc, p, tp, wi, st, cur, t, pl, kbuf, vbuf, row_lo, row_hi, lane, wave);
-  // products of the last tile (its V copy was waited for at its barrier),
-  // after the rescale its softmax may have asked for; the wait states first:
-  // the loop's products are instructions the compiler does not see as MFMAs
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  if (pc.any) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) ws.o[db][qb] *= pc.alpha[qb];
-  }
-  if ((tp.n - 1) & 1)
-    pv_products<D>(ws, pc.pp, vbuf[1], pl.vb0);
-  else
-    pv_products<D>(ws, pc.pp, vbuf[0], pl.vb0);
-
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int wrow = 64 * wave + 32 * qb + (lane & 31);
-    const long long orow = ((long long)wi.b * p.Sq + wi.qlocal0 + wrow) * p.Hq + wi.h;
-    finish_rows<D, kQB>(p, ws.o, qb, ws.m_ref[qb], ws.l_part[qb], wrow < wi.qrows, orow, lane);
-  }
-}
-
 template <int D>
 hipError_t launch(const StepParams& p, hipStream_t s) {
   const dim3 grid(8 * p.per_xcd);
   if constexpr (D == 128) {
-    if (p.pipe) {
-      if (p.mask_ext)
-        hipLaunchKernelGGL((attn_step_bf16_pipe_kernel<D, true>), grid, dim3(kThreads), 0, s, p);
-      else
-        hipLaunchKernelGGL((attn_step_bf16_pipe_kernel<D, false>), grid, dim3(kThreads), 0, s, p);
-      return hipGetLastError();
-    }
     if (p.ksplit) {
       if (p.mask_ext)
         hipLaunchKernelGGL((attn_step_bf16_ks_kernel<D, true, true>), grid, dim3(2 * kThreads), 0, s, p);

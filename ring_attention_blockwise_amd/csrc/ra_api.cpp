@@ -321,7 +321,6 @@ bool build_params(const ra_step_desc* d, const void* q, const void* k, const voi
       p->ksplit = (items < 2 * (int64_t)n_cus || (items < 4 * (int64_t)n_cus && unequal)) ? 1 : 0;
     }
   }
-  p->pipe = (d->dtype == RA_DTYPE_BF16 && d->D == 128 && !p->ksplit) ? 1 : 0;
   const int bq = ra::step_rows(d->dtype);
   p->qt_span0 = (int)((p->qs_len[0] + bq - 1) / bq);
   p->n_qtiles = p->qt_span0 + (int)((p->qs_len[1] + bq - 1) / bq);
@@ -683,7 +682,6 @@ int ra_rank_launches(const ra_rank_desc* d, const ra_mask* m, int32_t backward, 
       ra::StepParams p;
       if (ring.s_loc == 0 || !ring.forward_step(s, n_cus, &p)) continue;
       li.kernel = d->dtype == RA_DTYPE_F32 ? RA_KERNEL_STEP_F32
-                  : p.pipe                 ? RA_KERNEL_STEP_BF16_PIPE
                   : p.ksplit               ? RA_KERNEL_STEP_BF16_KSPLIT
                                            : RA_KERNEL_STEP_BF16;
       li.masked = p.mask_ext;

@@ -45,7 +45,6 @@ struct StepParams {
   int lpt;                  // 1: each XCD's items are whole heads, walked heaviest tile first across them
   int first_heavy;          // 1: the first query tiles see the most keys (walk them first)
   int ksplit;               // bf16, D = 128: eight-wave workgroups splitting each item's key tiles
-  int pipe;                 // bf16, D = 128: the software-pipelined kernel (one workgroup per CU)
 };
 
 // dtype: 0 = f32, 1 = bf16; D in {64, 128}.  The work decomposition of p

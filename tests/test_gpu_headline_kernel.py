@@ -1,7 +1,7 @@
 """Every-row parity of the kernels that produce the benchmark figures.
 
-The full-size rings run the bf16 D = 128 step kernel that the host picks for
-launches with many work items (at least two query tiles per CU).  The
+The full-size rings run the bf16 D = 128 four-wave step kernel, which the host
+picks for launches with many work items (at least two query tiles per CU).  The
 reduced rings below are sized so that the host picks that same kernel, and
 each test first asks the library (``ra_rank_launches``, with the device's own
 compute-unit count) which kernel every step launches and asserts it, so a
@@ -21,7 +21,7 @@ from ra_testlib import RankCase, assert_close, say, to_device
 
 pytestmark = pytest.mark.gpu
 
-PIPE = "step_bf16_pipe"
+FOUR_WAVE = "step_bf16"
 
 
 @pytest.fixture(scope="module")
@@ -83,7 +83,7 @@ RINGS = [
 
 
 @pytest.mark.parametrize("cfg", RINGS, ids=[c[0] for c in RINGS])
-def test_pipelined_kernel_every_row(ra, cfg):
+def test_four_wave_kernel_every_row(ra, cfg):
     label, B, Hq, Hkv, S, P, order, causal, k_scale, window, cu, ranks = cfg
     case = RankCase(900 + len(label), "bf16", B, Hq, Hkv, 128, S, P, order, causal, k_scale)
     for r in ranks:
@@ -91,7 +91,7 @@ def test_pipelined_kernel_every_row(ra, cfg):
         kinds = [s["kernel"] for s in plan]
         say(label, "rank", r, "kernels", kinds)
         launched = [k for k in kinds if k != "none"]
-        assert launched and all(k == PIPE for k in launched), kinds
+        assert launched and all(k == FOUR_WAVE for k in launched), kinds
         assert all(s["masked"] == bool(window or cu) for s in plan if s["kernel"] != "none")
         if window or cu is not None:
             o, lse = run_masked(ra, case, r, window, cu)

@@ -93,17 +93,16 @@ def test_launches_follow_the_pair_classes(name):
                 assert (plan[s]["kernel"] != "none") == (sees or (s == 0 and not backward)), (r, s, classes)
 
 
-def test_benchmark_workloads_take_the_pipelined_kernel():
-    """The 131k, 64k and 524k rings launch the software-pipelined step
-    kernel on every step, and the fused dK/dV backward; the 32k ring's
-    steps (256 query tiles with work: one per CU) take the key-split
-    kernel."""
+def test_benchmark_workloads_take_the_four_wave_kernel():
+    """The 131k, 64k and 524k rings launch the four-wave step kernel on
+    every step, and the fused dK/dV backward; the 32k ring's steps (256
+    query tiles with work: one per CU) take the key-split kernel."""
     for name in ("bf16_gqa32x8_d128_s128k_ring16_zigzag_causal", "bf16_mha16_b2_d128_s64k_ring8_contiguous_full",
                  "bf16_gqa32x8_d128_s512k_ring32_zigzag_causal_khalf"):
         w = WORKLOADS[name]
         kw = dict(dtype=w.dtype, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, S=w.S, P=w.P, rank=0, order=w.order,
                   causal=w.causal, n_cus=256)
-        assert {s["kernel"] for s in ra.ra_rank_launches(**kw)} == {"step_bf16_pipe"}, name
+        assert {s["kernel"] for s in ra.ra_rank_launches(**kw)} == {"step_bf16"}, name
         assert {s["kernel"] for s in ra.ra_rank_launches(backward=True, **kw)} == {"bwd_fused"}, name
     w = WORKLOADS["bf16_gqa32x8_d128_s32k_ring8_zigzag_causal"]
     plan = ra.ra_rank_launches(dtype=w.dtype, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, S=w.S, P=w.P, rank=0,
@@ -119,9 +118,9 @@ def test_launches_masked_instantiation():
     kw = dict(dtype="bf16", B=16, Hq=16, Hkv=4, D=128, S=4096, P=2, rank=0, order="zigzag", causal=True,
               n_cus=256)
     plan = ra.ra_rank_launches(window=1500, **kw)
-    assert [(s["kernel"], s["masked"]) for s in plan] == [("step_bf16_pipe", True)] * 2
+    assert [(s["kernel"], s["masked"]) for s in plan] == [("step_bf16", True)] * 2
     plan = ra.ra_rank_launches(**kw)
-    assert [(s["kernel"], s["masked"]) for s in plan] == [("step_bf16_pipe", False)] * 2
+    assert [(s["kernel"], s["masked"]) for s in plan] == [("step_bf16", False)] * 2
     # a one-key window cannot reach the held block of step 1 (keys
     # [1024, 3072), rank 0 holds rows [0, 1024) and [3072, 4096)): no launch
     plan = ra.ra_rank_launches(window=1, **kw)
