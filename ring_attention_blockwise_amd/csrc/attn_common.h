@@ -31,6 +31,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 // 2^kTau, so most tiles skip the rescale of O; the final division by the row
 // sum makes the result independent of where the reference sits.
 constexpr float kTau = 8.0f;
+constexpr float kTauSum = 256.0f;  // 2^kTau
+// A reference (in log2 units) for a row that has seen no visible key yet: any
+// finite score is more than kTau above it, and exp2 of its distance to any
+// such score is 0, while a masked score's exponent stays -inf (no inf - inf).
+constexpr float kMbNone = -0x1p100f;
 
 __device__ inline float max_halves(float x) {
   // v_permlane32_swap with both operands x: every lane sees x of lane ^ 32 in
@@ -324,13 +329,14 @@ __device__ inline void store_identity(const StepParams& p, const WorkItem& wi) {
 }
 
 // Epilogue of 32-row block qb held by a wave: O^T accumulators oq[D/32][qb]
-// (already complete over the block's keys), the reference maximum m_ref of
-// the raw scores and this lane's share of the row sum.  INIT stores O / l and
+// (already complete over the block's keys), the reference maximum mb of the
+// scores in log2 units (raw maximum times scale log2(e)) and this lane's
+// share of the row sum.  INIT stores O / l and
 // the LSE; ACCUM merges them into the (O, LSE) already in HBM (a stored LSE of
 // -inf is the identity and is replaced); a row that saw no visible key stores
 // the identity in INIT and is left alone in ACCUM.
 template <int D, int NQB>
-__device__ inline void finish_rows(const StepParams& p, const f32x16 (*oq)[NQB], int qb, float m_ref, float l_part,
+__device__ inline void finish_rows(const StepParams& p, const f32x16 (*oq)[NQB], int qb, float mb, float l_part,
                                    bool row_ok, long long orow, int lane) {
   const int dsub = 4 * (lane >> 5);
   const float l_tot = sum_halves(l_part);
@@ -338,7 +344,7 @@ __device__ inline void finish_rows(const StepParams& p, const f32x16 (*oq)[NQB],
   float* orow_ptr = p.o + orow * D;
   if (l_tot > 0.f) {
     const float inv = 1.f / l_tot;
-    const float lse_s = m_ref * p.scale + __builtin_amdgcn_logf(l_tot) * kLn2;
+    const float lse_s = (mb + __builtin_amdgcn_logf(l_tot)) * kLn2;
     float lse_r = kNegInf;
     if (p.accum) lse_r = p.lse[orow];
     if (lse_r == kNegInf) {

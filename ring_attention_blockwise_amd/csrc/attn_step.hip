@@ -240,7 +240,7 @@ void attn_step_f32_kernel(StepParams p) {
   }
   if (t < tp.n) step_tile<D, 0>(ws, p, tp, st, wi, cur, t, kbuf, vbuf, row_lo, row_hi, lane);
 
-  finish_rows<D, 1>(p, ws.o, 0, ws.m_ref, ws.l_part, row_ok, orow, lane);
+  finish_rows<D, 1>(p, ws.o, 0, ws.m_ref * p.sl2, ws.l_part, row_ok, orow, lane);
 }
 
 template <int D>

@@ -54,6 +54,7 @@ using namespace dev;
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kQB = 2;         // 32-row query blocks per wave
@@ -87,7 +88,7 @@ template <int D>
 struct WaveState {
   bf16x8 q[kQB][D / 16];      // Q^T operands: Q[row][16u + 8(l/32) .. +7]
   f32x16 o[D / 32][kQB];      // O^T accumulators
-  float m_ref[kQB];           // reference maximum of the raw scores
+  float mb[kQB];              // reference maximum times scale log2(e); kMbNone before any key
   float l_part[kQB];          // this lane's share of the row sum
 };
 
@@ -132,14 +133,18 @@ struct Lane {
   }
 };
 
-// DMA staging of K and V tiles for one work item.
-template <int D>
+// DMA staging of K and V tiles for one work item.  kLazy: the lane's chunk
+// offsets are derived again at each copy (from a laundered thread id) instead
+// of being held in registers across the loop; the eight-wave kernel and the
+// masked instantiations, whose loops carry a few more values, need those
+// registers.
+template <int D, bool kLazy>
 struct Stager {
   typedef Layout<D> Ly;
   const char* khead;   // row 0 of this (batch, kv head) in K
   const char* vhead;
   unsigned row_bytes;
-  unsigned ko[Ly::kDma], vo[Ly::kDma];  // this lane's chunk offsets in a tile
+  unsigned ko[kLazy ? 1 : Ly::kDma], vo[kLazy ? 1 : Ly::kDma];  // this lane's chunk offsets in a tile
   int wave;
 
   __device__ void init(const StepParams& p, const WorkItem& wi, const Lane<D>& ln) {
@@ -148,10 +153,12 @@ struct Stager {
     khead = (const char*)p.k + head;
     vhead = (const char*)p.v + head;
     wave = ln.wave;
+    if (!kLazy) {
 #pragma unroll
-    for (int i = 0; i < Ly::kDma; ++i) {
-      ko[i] = ln.dma_offset(i, false);
-      vo[i] = ln.dma_offset(i, true);
+      for (int i = 0; i < Ly::kDma; ++i) {
+        ko[i] = ln.dma_offset(i, false);
+        vo[i] = ln.dma_offset(i, true);
+      }
     }
   }
 
@@ -166,8 +173,17 @@ struct Stager {
     for (int i = 0; i < Ly::kDma; ++i) {
       RA_LDS char* kd = kdst + (wave * Ly::kDma + i) * 1024;
       RA_LDS char* vd = vdst + (wave * Ly::kDma + i) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (RA_LDS void*)kd, 16, (int)ko[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (RA_LDS void*)vd, 16, (int)vo[i], 0, 0, 0);
+      unsigned kof, vof;
+      if (kLazy) {
+        const Lane<D> ln(row_bytes, wave);
+        kof = ln.dma_offset(i, false);
+        vof = ln.dma_offset(i, true);
+      } else {
+        kof = ko[i];
+        vof = vo[i];
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (RA_LDS void*)kd, 16, (int)kof, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (RA_LDS void*)vd, 16, (int)vof, 0, 0, 0);
     }
   }
 };
@@ -183,7 +199,7 @@ __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "mem
 // two wave sets sharing each SIMD this is.
 template <int D, int PAR, bool kExt, bool kKS>
 __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const TilePlan& tp, const WorkItem& wi,
-                                 const Stager<D>& st, TileCursor& cur, int t, int te, unsigned phase,
+                                 const Stager<D, kKS || kExt>& st, TileCursor& cur, int t, int te, unsigned phase,
                                  RA_LDS char* const* kbuf, RA_LDS char* const* vbuf, const RA_LDS int* row_lo,
                                  const RA_LDS int* row_hi, int lane, int wave) {
   if (kKS && t >= te) {
@@ -207,35 +223,27 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
     st.issue(cur, kbuf[PAR ^ 1], vbuf[PAR ^ 1]);
   }
 
-  // S^T = K Q^T
-  const unsigned kb0 = ln.kb0();
+  // S^T = K Q^T; masked: (tiles past the unmasked ones only; a uniform
+  // branch) the keys of the tile each row may not see are set to -inf: keys
+  // below lim (the causal diagonal, a span's ragged end, a packed sequence's
+  // end) and, with a window or packed sequences, from lo on are visible.  The
+  // sign bit of each distance selects -inf with a bitfield insert (no compare
+  // masks, which would take scalar registers).
   f32x16 s[kQB];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) s[qb] = f32x16{};
-#pragma unroll
-  for (int u = 0; u < D / 16; ++u) {
-    const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(kbuf[PAR], kb0 ^ (32u * u)));
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.q[qb][u], s[qb], 0, 0, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-  for (int u = 2; u < D / 16; ++u) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-
-  __builtin_amdgcn_sched_barrier(0);
-  // mask (tiles past the unmasked ones only; a uniform branch): key k of
-  // the tile is visible to row q iff k < lim(q)
   const int L = lane >> 5;
-  if (ti.masked()) {
-    // keys of the tile visible to the row: below lim (the causal diagonal, a
-    // span's ragged end, a packed sequence's end) and, with a window or
-    // packed sequences, from lo on.  The sign bit of each distance selects
-    // -inf with a bitfield insert (no compare masks, which would take scalar
-    // registers).
+  auto scores = [&]() {
+    const unsigned kb0 = ln.kb0();
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) s[qb] = f32x16{};
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(kbuf[PAR], kb0 ^ (32u * u)));
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.q[qb][u], s[qb], 0, 0, 0);
+    }
+  };
+  auto mask = [&]() {
+    if (!ti.masked()) return;
     const long long d0 = wi.qglob0 - ti.glob0 + 1;
     const int dc = p.causal ? (int)max(-1024LL, min(1024LL, d0)) : 1024;
     const int base = kExt ? (int)max(-(1LL << 30), min(1LL << 30, ti.glob0 - wi.qglob0)) : 0;
@@ -258,57 +266,84 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
         s[qb][r] = __uint_as_float((m & 0xff800000u) | (~m & __float_as_uint(s[qb][r])));
       }
     }
+  };
+  scores();
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int u = 2; u < D / 16; ++u) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-
-  // running maximum; rescale only when it grows by more than 2^kTau
-  bool grow[kQB];
-  bool any = false;
-  float m_new[kQB];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    float tmax = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[qb][r]);
-    tmax = max_halves(tmax);
-    m_new[qb] = fmaxf(ws.m_ref[qb], tmax);
-    // -inf reference: the difference is +inf and the maximum is taken;
-    // both -inf: NaN compares false and nothing moves.
-    grow[qb] = (m_new[qb] - ws.m_ref[qb]) * p.sl2 > kTau;
-    any |= grow[qb];
-  }
-  if (__builtin_amdgcn_ballot_w64(any)) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const float alpha = grow[qb] ? __builtin_amdgcn_exp2f((ws.m_ref[qb] - m_new[qb]) * p.sl2) : 1.f;
-      if (grow[qb]) ws.m_ref[qb] = m_new[qb];
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) ws.o[db][qb] *= alpha;
-      ws.l_part[qb] *= alpha;
-    }
-  }
-
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   __builtin_amdgcn_sched_barrier(0);
-  // P = exp2(S sl2 - m sl2), rounded to bf16 as the B operand of O^T += V^T P^T
+  mask();
+
+  // P = exp2(S sl2 - mb) against the row's current reference mb (log2
+  // units), rounded to bf16 as the B operand of O^T += V^T P^T, and this
+  // lane's share of the tile's row sum, which adds the rounded probabilities
+  // (the weights the products apply) two at a time: v_dot2 with a pair of
+  // ones.  A masked score gives 0.
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   bf16x8 pb[kQB][2];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const float mb = ws.m_ref[qb] == kNegInf ? 0.f : ws.m_ref[qb] * p.sl2;
-    float lsum = 0.f;
+  float lt[kQB];
+  auto probabilities = [&](int qb) {
+    lt[qb] = 0.f;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       f32x8 x;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * hf + e], p.sl2, -mb));
-        lsum += x[e];
-      }
+      for (int e = 0; e < 8; ++e) x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * hf + e], p.sl2, -ws.mb[qb]));
       pb[qb][hf] = __builtin_convertvector(x, bf16x8);
+      const u32x4 pw = __builtin_bit_cast(u32x4, pb[qb][hf]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // the element goes through a scalar: a bit cast taken straight from
+        // pw[e] compiles to element 0 for every e with this compiler
+        const unsigned w = pw[e];
+        lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, lt[qb], false);
+      }
       // one 8-key group at a time keeps the exponentials' temporaries few
       __builtin_amdgcn_sched_barrier(0);
     }
-    ws.l_part[qb] += lsum;
-    // materialise the row sum here: otherwise the adds sink into the next
-    // tile and keep this tile's 32 probabilities alive across it
+  };
+  bool over = false;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    probabilities(qb);
+    over |= !(lt[qb] <= kTauSum);
+  }
+  // A lane's tile sum bounds each of its probabilities, so while no sum
+  // passes 2^kTau every P is at most 2^kTau and the reference stays (the
+  // common case).  Otherwise (the first visible tile, where mb is still
+  // kMbNone, or scores that grew) the scores are formed again from the K
+  // tile, still in LDS (keeping them alive under the probabilities would
+  // not fit the registers), the rows whose tile maximum lies more than kTau
+  // above the reference move it there, O and l are rescaled, and the
+  // probabilities are taken again.
+  if (__builtin_amdgcn_ballot_w64(over)) {
+    scores();
+    mask();
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      float t = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t = fmaxf(t, s[qb][r]);
+      const float mb = max_halves(t) * p.sl2;
+      if (mb - ws.mb[qb] > kTau) {
+        const float alpha = __builtin_amdgcn_exp2f(ws.mb[qb] - mb);
+        ws.mb[qb] = mb;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) ws.o[db][qb] *= alpha;
+        ws.l_part[qb] *= alpha;
+      }
+      probabilities(qb);
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    ws.l_part[qb] += lt[qb];
+    // materialise the row sum here: otherwise the sums sink into the next
+    // tile and keep this tile's probabilities alive across it
     asm volatile("" : "+v"(ws.l_part[qb]));
   }
 
@@ -347,7 +382,7 @@ __device__ __attribute__((always_inline)) inline void fwd_pass(WaveState<D>& ws,
                                                                int iters, unsigned phase, RA_LDS char* const* kbuf,
                                                                RA_LDS char* const* vbuf, const RA_LDS int* row_lo,
                                                                const RA_LDS int* row_hi, int lane, int wave) {
-  Stager<D> st;
+  Stager<D, kKS || kExt> st;
   st.init(p, wi, Lane<D>((unsigned)(p.Hkv * D * 2), wave));
   TileCursor cur;
   cur.first(tp);
@@ -363,7 +398,7 @@ __device__ __attribute__((always_inline)) inline void fwd_pass(WaveState<D>& ws,
       ws.q[qb][u] = wrow < wi.qrows ? *(const bf16x8*)(qrow + 16 * u + 8 * (lane >> 5)) : bf16x8{};
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) ws.o[db][qb] = f32x16{};
-    ws.m_ref[qb] = kNegInf;
+    ws.mb[qb] = kMbNone;
     ws.l_part[qb] = 0.f;
   }
   wait_loads();
@@ -425,7 +460,7 @@ void attn_step_bf16_kernel(StepParams p) {
   }
 
   // prologue: tile 0 in flight while Q is read
-  Stager<D> st;
+  Stager<D, kExt> st;
   st.init(p, wi, Lane<D>((unsigned)(p.Hkv * D * 2), wave));
   TileCursor cur;
   cur.first(tp);
@@ -441,7 +476,7 @@ void attn_step_bf16_kernel(StepParams p) {
       ws.q[qb][u] = wrow < wi.qrows ? *(const bf16x8*)(qrow + 16 * u + 8 * (lane >> 5)) : bf16x8{};
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) ws.o[db][qb] = f32x16{};
-    ws.m_ref[qb] = kNegInf;
+    ws.mb[qb] = kMbNone;
     ws.l_part[qb] = 0.f;
   }
   wait_loads();
@@ -461,7 +496,7 @@ void attn_step_bf16_kernel(StepParams p) {
   for (int qb = 0; qb < kQB; ++qb) {
     const int wrow = 64 * wave + 32 * qb + (lane & 31);
     const long long orow = ((long long)wi.b * p.Sq + wi.qlocal0 + wrow) * p.Hq + wi.h;
-    finish_rows<D, kQB>(p, ws.o, qb, ws.m_ref[qb], ws.l_part[qb], wrow < wi.qrows, orow, lane);
+    finish_rows<D, kQB>(p, ws.o, qb, ws.mb[qb], ws.l_part[qb], wrow < wi.qrows, orow, lane);
   }
 }
 
@@ -543,7 +578,7 @@ void attn_step_bf16_ks_kernel(StepParams p) {
         if (r == 0) {
 #pragma unroll
           for (int qb = 0; qb < kQB; ++qb) {
-            xm[qb] = ws.m_ref[qb];
+            xm[qb] = ws.mb[qb];
             xm[kQB + qb] = ws.l_part[qb];
           }
         }
@@ -564,12 +599,14 @@ void attn_step_bf16_ks_kernel(StepParams p) {
         if (r == 0) {
 #pragma unroll
           for (int qb = 0; qb < kQB; ++qb) {
-            const float m0 = ws.m_ref[qb], m1 = xm[qb];
+            // a set that saw no key has kMbNone, far below the other's reference
+            // (a = 0), or both have it and l = 0
+            const float m0 = ws.mb[qb], m1 = xm[qb];
             const float m = fmaxf(m0, m1);
-            a0[qb] = m0 == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m0 - m) * p.sl2);
-            a1[qb] = m1 == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * p.sl2);
+            a0[qb] = __builtin_amdgcn_exp2f(m0 - m);
+            a1[qb] = __builtin_amdgcn_exp2f(m1 - m);
             ws.l_part[qb] = a0[qb] * ws.l_part[qb] + a1[qb] * xm[kQB + qb];
-            ws.m_ref[qb] = m;
+            ws.mb[qb] = m;
           }
         }
 #pragma unroll
@@ -594,7 +631,7 @@ void attn_step_bf16_ks_kernel(StepParams p) {
   for (int qb = 0; qb < kQB; ++qb) {
     const int wrow = 64 * wave + 32 * qb + (lane & 31);
     const long long orow = ((long long)wi.b * p.Sq + wi.qlocal0 + wrow) * p.Hq + wi.h;
-    finish_rows<D, kQB>(p, ws.o, qb, ws.m_ref[qb], ws.l_part[qb], wrow < wi.qrows, orow, lane);
+    finish_rows<D, kQB>(p, ws.o, qb, ws.mb[qb], ws.l_part[qb], wrow < wi.qrows, orow, lane);
   }
 }
 
