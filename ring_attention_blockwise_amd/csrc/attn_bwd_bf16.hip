@@ -13,25 +13,29 @@
 //   dQ += scale dS K,  dK += scale dS^T Q,  dV += P^T dO,
 // with the G query heads of a group adding into their shared K/V head.
 //
-// Three kernels; in none of them do two workgroups add into the same rows:
+// The kernels; in none of them do two workgroups add into the same rows:
 //   * dQ: a workgroup (4 waves) owns 128 query rows of one (batch, query
 //     head), 32 per wave, and walks the step's key tiles like the forward
 //     kernel: S^T = K Q^T and dP^T = V dO^T (K, V rows from LDS, Q^T and dO^T
 //     in registers), then dQ^T += K^T dS^T with K^T gathered by transposing
 //     LDS reads.
-//   * dV and dK (two kernels of one template): a workgroup owns 128 keys of
-//     one (batch, kv head), 32 per wave, with K^T (and for dK V^T) in
-//     registers for the whole item, and walks the query tiles (32 rows) of
-//     every query head of the group that see them: S = Q K^T (Q rows from
-//     LDS), then dV^T += dO^T P; or S and dP = dO V^T, then dK^T += Q^T dS,
-//     with dO^T, Q^T by transposing LDS reads.  Fused, the two need about 290
-//     registers (one wave per SIMD); split, about 155 and 210 (two per SIMD),
-//     for one more product (S twice).  The softmax rows are spread over the
-//     accumulator registers here, so the rows' L and delta come from LDS as 16
-//     values per lane.  When a launch's key tiles carry very unequal work
-//     (causal, windowed diagonals), eight-wave workgroups let two groups of
-//     four waves share a key tile's query tiles; the second group hands its
-//     partial sums to the first through LDS.
+//   * dK and dV, fused (the default): an eight-wave workgroup owns 128 keys
+//     of one (batch, kv head) and walks the query tiles (32 rows) of every
+//     query head of the group that see them.  Waves 0..3 (32 keys each, K^T
+//     and V^T in registers for the whole item) form S = Q K^T and dP = dO V^T
+//     and add dK^T += Q^T dS, and they leave each query tile's P, rounded to
+//     bf16, in LDS; waves 4..7 add dV^T += dO^T P one query tile behind, from
+//     that P and the tile's dO while it is still staged (three stages of Q,
+//     dO, L and P).  The dV waves recompute neither S nor P.  One wave holding
+//     both accumulators would need about 290 registers (one wave per SIMD);
+//     split over two waves of a SIMD they fit.
+//   * dV and dK, separate (two kernels of one template), for launches whose
+//     key tiles would not give every CU a workgroup: the same walk, S formed
+//     in both; eight-wave workgroups let two groups of four waves share a key
+//     tile's query tiles, the second handing its partial sums to the first
+//     through LDS.
+// The softmax rows are spread over the accumulator registers in the dK/dV
+// kernels, so the rows' L and delta come from LDS as 16 values per lane.
 // Tiles are copied global -> LDS by buffer loads with the LDS bit.  One LDS
 // layout serves both read patterns: chunk c of row r sits at c ^ csw(r), with
 // csw(r) = 4 (r mod 4) + (r / 4) mod 4, which keeps the 16 rows of a row read

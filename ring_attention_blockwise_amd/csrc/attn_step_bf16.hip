@@ -208,6 +208,11 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
   }
   const Lane<D> ln((unsigned)(p.Hkv * D * 2), wave);
   const TileCursor ti = cur;
+  // the scores' first two K operands are read before the scalar work of the
+  // next tile's copy, which then covers their latency
+  const unsigned kb0 = ln.kb0();
+  const bf16x8 a0 = __builtin_bit_cast(bf16x8, lds_load16(kbuf[PAR], kb0));
+  const bf16x8 a1 = __builtin_bit_cast(bf16x8, lds_load16(kbuf[PAR], kb0 ^ 32u));
   // Two wave sets share each SIMD (two workgroups of a CU, or the two groups
   // of an eight-wave workgroup); the wave arbiter favours the older, which
   // then finishes its (equal) work long before the younger.  Swapping the
@@ -231,13 +236,14 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
   // masks, which would take scalar registers).
   f32x16 s[kQB];
   const int L = lane >> 5;
-  auto scores = [&]() {
-    const unsigned kb0 = ln.kb0();
+  auto scores = [&](bool first) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) s[qb] = f32x16{};
 #pragma unroll
     for (int u = 0; u < D / 16; ++u) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(kbuf[PAR], kb0 ^ (32u * u)));
+      const bf16x8 a = first && u == 0   ? a0
+                       : first && u == 1 ? a1
+                                         : __builtin_bit_cast(bf16x8, lds_load16(kbuf[PAR], kb0 ^ (32u * u)));
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.q[qb][u], s[qb], 0, 0, 0);
     }
@@ -267,8 +273,7 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
       }
     }
   };
-  scores();
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  scores(true);
 #pragma unroll
   for (int u = 2; u < D / 16; ++u) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -321,7 +326,7 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
   // above the reference move it there, O and l are rescaled, and the
   // probabilities are taken again.
   if (__builtin_amdgcn_ballot_w64(over)) {
-    scores();
+    scores(false);
     mask();
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
