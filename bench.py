@@ -638,6 +638,124 @@ def cpu_aux_baselines(w, rank):
     return out
 
 
+# --------------------------------------------------------------------------
+# Summaries of rocprofv3 output (host only: they read the CSV files a profiled
+# run of this script wrote, and print or write the figures kept in profiles/).
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(dict(r, _file=f) for r in csv.DictReader(fh))
+    return rows
+
+
+def _short_kernel(name):
+    """Kernel name without 'void ', namespaces and the parameter list."""
+    n = name.strip()
+    if n.startswith("void "):
+        n = n[5:]
+    depth, cut = 0, len(n)
+    for i, c in enumerate(n):   # the parameter list is the last top-level '(...)'
+        if c == "<":
+            depth += 1
+        elif c == ">":
+            depth -= 1
+        elif c == "(" and depth == 0:
+            cut = i
+    n = n[:cut]
+    for ns in ("ra::(anonymous namespace)::", "ra::"):
+        n = n.replace(ns, "")
+    return n
+
+
+def trace_summary(d, warmup, steps, kernel=KERNEL_NAME):
+    """Markdown table of a --kernel-trace run of this script (``--no-aux``):
+    every kernel's launches, and the step kernel's average over the timed
+    dispatches only.  The script launches the step kernel per ring step in
+    this order: ``warmup`` untimed steps, ``steps`` timed steps, then the
+    per-launch leg's one untimed and ``steps`` timed repetitions."""
+    rows = _csv_rows(d, "kernel_trace.csv")
+    per = {}
+    for r in rows:
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per.setdefault(_short_kernel(r["Kernel_Name"]), []).append((int(r["Dispatch_Id"]), us))
+    total = sum(u for v in per.values() for _, u in v)
+    out = ["| kernel | calls | avg us | median us | min us | max us | share |", "|---|---|---|---|---|---|---|"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(u for _, u in kv[1])):
+        us = [u for _, u in v]
+        out.append(f"| `{k}` | {len(us)} | {np.mean(us):.1f} | {np.median(us):.1f} | {min(us):.1f} | "
+                   f"{max(us):.1f} | {100 * sum(us) / total:.2f}% |")
+    step = [u for _, u in sorted(per.get(kernel, []))]
+    reps = warmup + 2 * steps + 1
+    if step and len(step) % reps == 0:
+        n = len(step) // reps
+        ring = step[warmup * n:(warmup + steps) * n]
+        leg = step[(warmup + steps + 1) * n:]
+        out += ["", f"`{kernel}`: {n} launches per ring step; {len(step)} dispatches = ({warmup} untimed + "
+                f"{steps} timed ring steps + 1 untimed + {steps} timed per-launch repetitions) x {n}.",
+                f"- timed ring steps: {len(ring)} dispatches, mean {np.mean(ring):.1f} us, median "
+                f"{np.median(ring):.1f} us, min {min(ring):.1f} us; {n} x mean = {n * np.mean(ring) / 1e3:.3f} ms "
+                f"of kernel time per ring step",
+                f"- timed per-launch repetitions: {len(leg)} dispatches, mean {np.mean(leg):.1f} us, median "
+                f"{np.median(leg):.1f} us"]
+    return "\n".join(out)
+
+
+def counter_means(dirs, kernel=KERNEL_NAME):
+    """Mean per dispatch of every counter of ``kernel`` in rocprofv3
+    --pmc CSVs under ``dirs`` (a counter read per instance is summed over
+    its instances first)."""
+    vals = {}
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if _short_kernel(r.get("Kernel_Name", "")) != kernel:
+                continue
+            key = (r["_file"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            vals.setdefault(r["Counter_Name"], {}).setdefault(key, 0.0)
+            vals[r["Counter_Name"]][key] += float(r["Counter_Value"])
+    return {c: (float(np.mean(list(v.values()))), len(v)) for c, v in sorted(vals.items())}
+
+
+def counter_summary(dirs, kernel=KERNEL_NAME):
+    out = [f"`{kernel}`, mean per dispatch:", "", "| counter | per dispatch | dispatches |", "|---|---|---|"]
+    for c, (m, n) in counter_means(dirs, kernel).items():
+        out.append(f"| {c} | {m:.4e} | {n} |")
+    return "\n".join(out)
+
+
+def traffic_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload_name, commands):
+    """HBM bytes per launch of the step kernel from FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for the
+    plain 1 GiB device copy of ``--copy-calib``; the record carries the hash
+    of the kernel's sources it was taken on."""
+    def mean_of(d, counter, kernel):
+        m = counter_means([d], kernel).get(counter)
+        return m
+
+    def copy_kib(d, counter):
+        v = []
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] == counter and "copy" in r.get("Kernel_Name", "").lower():
+                v.append(float(r["Counter_Value"]))
+        return float(np.median(v))
+
+    f_raw, nf = mean_of(fetch_dir, "FETCH_SIZE", KERNEL_NAME)
+    w_raw, nw = mean_of(write_dir, "WRITE_SIZE", KERNEL_NAME)
+    cf, cw = copy_kib(cal_fetch_dir, "FETCH_SIZE"), copy_kib(cal_write_dir, "WRITE_SIZE")
+    fs, ws = (1 << 30) / (cf * 1024), (1 << 30) / (cw * 1024)
+    rec = {"workload": workload_name, "kernel": KERNEL_NAME, "kernel_hash": kernel_hash(), "commands": commands,
+           "launches_sampled": min(nf, nw), "fetch_kib_per_launch_raw": round(f_raw, 1),
+           "write_kib_per_launch_raw": round(w_raw, 1),
+           "calibration": {"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "fetch_kib_raw": round(cf, 1),
+                           "write_kib_raw": round(cw, 1), "fetch_scale": round(fs, 5), "write_scale": round(ws, 5)},
+           "fetch_bytes_per_launch": int(f_raw * 1024 * fs), "write_bytes_per_launch": int(w_raw * 1024 * ws)}
+    rec["bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -650,7 +768,31 @@ def main():
     ap.add_argument("--no-clock", action="store_true", help="skip sampling the GFX clock under load")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (scale reference for HBM byte counters)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print the kernel table of a rocprofv3 --kernel-trace run of this script (--steps and "
+                         "--warmup as that run's) and exit; no GPU")
+    ap.add_argument("--counter-summary", metavar="DIR", nargs="+",
+                    help="print the step kernel's mean counters from rocprofv3 --pmc runs and exit; no GPU")
+    ap.add_argument("--kernel", default=KERNEL_NAME, help="kernel the summaries take (short name)")
+    ap.add_argument("--traffic-summary", metavar="DIR", nargs=4,
+                    help="FETCH_SIZE, WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE run directories: write the "
+                         "HBM traffic record and exit; no GPU")
+    ap.add_argument("--traffic-commands", nargs="*", default=[], help="the commands of the four runs, recorded")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.warmup, args.steps, args.kernel))
+        return
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary, args.kernel))
+        return
+    if args.traffic_summary:
+        from seeded_inputs.workloads import HEADLINE
+        rec = traffic_summary(*args.traffic_summary, args.workload or HEADLINE, args.traffic_commands)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one rank's ring steps on one GPU; --gpus {args.gpus} is not "
               "supported (the ring's other ranks are simulated on this GPU, and no collective "
