@@ -657,15 +657,13 @@ def _short_kernel(name):
     n = name.strip()
     if n.startswith("void "):
         n = n[5:]
-    depth, cut = 0, len(n)
-    for i, c in enumerate(n):   # the parameter list is the last top-level '(...)'
-        if c == "<":
-            depth += 1
-        elif c == ">":
-            depth -= 1
-        elif c == "(" and depth == 0:
-            cut = i
-    n = n[:cut]
+    if n.endswith(")"):         # the parameter list: the '(...)' that ends the name
+        depth = 0
+        for i in range(len(n) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(n[i], 0)
+            if depth == 0:
+                n = n[:i]
+                break
     for ns in ("ra::(anonymous namespace)::", "ra::"):
         n = n.replace(ns, "")
     return n

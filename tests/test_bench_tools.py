@@ -28,6 +28,9 @@ def test_short_kernel_names():
             "at::native::and_kernel_cuda(at::TensorIterator&)::{lambda()#1}> > >(at::native::ReduceOp<bool>)")
     assert bench._short_kernel(long).startswith("at::native::reduce_kernel<512, 1,")
     assert not bench._short_kernel(long).endswith(")")
+    vec = ("void ra::(anonymous namespace)::relayout_kernel<unsigned int __vector(4)>(int, unsigned int, "
+           "unsigned int __vector(4) const*, unsigned int __vector(4)*)")
+    assert bench._short_kernel(vec) == "relayout_kernel<unsigned int __vector(4)>"
 
 
 def test_trace_summary_takes_only_timed_dispatches(tmp_path):
