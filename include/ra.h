@@ -222,7 +222,8 @@ int ra_allgather_forward(const ra_rank_desc* d, const void* q_local,
  *             zeroes them; running every rank into the same buffers gives the
  *             full gradients)
  *   delta     [B, S/P, Hq] float32: caller-provided workspace, written with
- *             rowsum(dout * o)
+ *             -rowsum(dout * o) (negated: the kernels start their dP
+ *             accumulation from it)
  * bf16 inputs with D = 128 run the tuned MFMA kernels (P and dS rounded to
  * bf16 before their products); float32 inputs, or D = 64, run plain SIMT
  * kernels in float32, meant for parity-scale problems.  Other requirements

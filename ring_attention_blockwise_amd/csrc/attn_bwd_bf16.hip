@@ -140,7 +140,9 @@ struct DqState {
   bf16x8 d[kD / 16];    // dO^T operand, same layout
   f32x16 acc[kD / 32];  // dQ^T accumulators
   float lse2;           // L * log2(e) of the lane's row (+inf: the row has no weight)
-  float dlt;            // delta of the lane's row
+  f32x16 ndl;           // -delta of the lane's row (the workspace's value) in
+                        // every element: dP^T's starting value, so the chain
+                        // yields dP - delta
 };
 
 template <int PAR, bool kExt>
@@ -163,7 +165,8 @@ __device__ inline void dq_tile(DqState& st, const BwdParams& bp, const TilePlan&
     stg.issue(cur, kbuf[PAR ^ 1], vbuf[PAR ^ 1]);
   }
   const unsigned rb = row_base_sigma(lane);
-  f32x16 s = f32x16{}, dp = f32x16{};
+  // S^T = K Q^T and dP^T - delta = V dO^T - delta (the chain starts from -delta)
+  f32x16 s = f32x16{}, dp = st.ndl;
 #pragma unroll
   for (int u = 0; u < kD / 16; ++u) {
     const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(kbuf[PAR], rb ^ (32u * u)));
@@ -193,6 +196,7 @@ __device__ inline void dq_tile(DqState& st, const BwdParams& bp, const TilePlan&
     }
   }
   // P^T = exp2(S^T sl2 - L log2 e); dS^T = P^T (dP^T - delta), rounded to bf16
+  // (dp holds dP^T - delta already)
   bf16x8 dsb[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
@@ -200,7 +204,7 @@ __device__ inline void dq_tile(DqState& st, const BwdParams& bp, const TilePlan&
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hf + e], p.sl2, -st.lse2));
-      x[e] = pr * (dp[8 * hf + e] - st.dlt);
+      x[e] = pr * dp[8 * hf + e];
     }
     dsb[hf] = __builtin_convertvector(x, bf16x8);
   }
@@ -281,7 +285,9 @@ void attn_bwd_dq_kernel(BwdParams bp) {
     for (int db = 0; db < kD / 32; ++db) st.acc[db] = f32x16{};
     const float l = row_ok ? bp.lse[orow] : kNegInf;
     st.lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
-    st.dlt = row_ok ? bp.delta[orow] : 0.f;
+    const float ndl = row_ok ? bp.delta[orow] : 0.f;  // the workspace holds -delta
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st.ndl[e] = ndl;
   }
   wait_loads();
   __syncthreads();
@@ -499,7 +505,21 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
   const bool live = has_keys && (!p.causal || kwg <= qglob + qcount - 1);
   if (live) {
     const unsigned rb = row_base_sigma(lane);
+    const int L = (int)(lane >> 5);
+    const RA_LDS float* lt = (const RA_LDS float*)lbuf[CUR];
+    // dP starts from the rows' -delta (staged with the tile; the workspace
+    // holds -delta), so the chain yields dP - delta: register r of the lane
+    // is row 16(r/8) + 8L + r%8
     f32x16 s = f32x16{}, dp = f32x16{};
+    if (kDK) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 t0 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L);
+        const f32x4 t1 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[8 * hf + e] = t0[e], dp[8 * hf + 4 + e] = t1[e];
+      }
+    }
 #pragma unroll
     for (int u = 0; u < kD / 16; ++u) {
       const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(qbuf[CUR], rb ^ (32u * u)));
@@ -511,7 +531,6 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
     }
     __builtin_amdgcn_sched_barrier(0);
     // rows of register r: 16(r/8) + 8L + r%8 of the tile
-    const int L = (int)(lane >> 5);
     const int key = (int)(lane & 31u);
     // window, packed sequences: row i sees key j iff lo_i <= j <= hi_i, the
     // row's range relative to the tile's first row (staged with the tile)
@@ -523,7 +542,6 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = neg_inf_select(dd + 16 * (r >> 3) + (r & 7), s[r]);
     }
-    const RA_LDS float* lt = (const RA_LDS float*)lbuf[CUR];
     unsigned b0, b1;
     tr_bases(lane, b0, b1);
     // one 16-row half at a time: P (and dS) of rows 16hf .. 16hf+15, then the
@@ -533,13 +551,6 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
       const f32x4 l0 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L);
       const f32x4 l1 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L + 4);
       const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-      float tv[8];
-      if (kDK) {
-        const f32x4 t0 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L);
-        const f32x4 t1 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L + 4);
-        tv[0] = t0[0], tv[1] = t0[1], tv[2] = t0[2], tv[3] = t0[3];
-        tv[4] = t1[0], tv[5] = t1[1], tv[6] = t1[2], tv[7] = t1[3];
-      }
       int lo[8], hi[8];
       if (kExt) {
         const i32x4 a0 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L);
@@ -560,7 +571,7 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
         float a = __builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e);
         if (kExt) a = (lo[e] <= dk && dk <= hi[e]) ? a : kNegInf;
         const float pr = __builtin_amdgcn_exp2f(a);
-        x[e] = kDK ? pr * (dp[8 * hf + e] - tv[e]) : pr;
+        x[e] = kDK ? pr * dp[8 * hf + e] : pr;
         if (kPOut) xp[e] = pr;
       }
       // P as the dV product takes it (the fused kernel's other wave group)
@@ -910,7 +921,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(long long rows, const T*
   }
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
-  if (row < rows && part == 0) delta[row] = acc;
+  // stored negated: the products start their dP accumulation from it
+  if (row < rows && part == 0) delta[row] = -acc;
 }
 
 }  // namespace

@@ -55,7 +55,7 @@ __device__ inline void wg_sum2(float& a, float& b, float* red) {
   b = red[1] + red[3];
 }
 
-// delta[row] = sum_d dO[row, d] O[row, d], one thread per row
+// delta[row] = -sum_d dO[row, d] O[row, d] (stored negated), one thread per row
 template <typename T, int D>
 __global__ __launch_bounds__(256) void simt_delta_kernel(long long rows, const T* __restrict__ dout,
                                                          const float* __restrict__ o, float* __restrict__ delta) {
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void simt_delta_kernel(long long rows, const T
   if (row >= rows) return;
   float acc = 0.f;
   for (int d = 0; d < D; ++d) acc += ld<T>(dout, row * D + d) * o[row * D + d];
-  delta[row] = acc;
+  delta[row] = -acc;
 }
 
 // grid: x = the step's listed query rows (span 0's, then span 1's), y = query
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(D) void simt_dq_kernel(BwdParams bp) {
   const int g = h / p.G;
   const float q = ld<T>((const T*)p.q, qrow * D + d);
   const float dov = ld<T>((const T*)bp.dout, qrow * D + d);
-  const float lse = bp.lse[qrow], dl = bp.delta[qrow];
+  const float lse = bp.lse[qrow], ndl = bp.delta[qrow];  // -delta
   const long long lo = key_lo(p, t), hi = key_hi(p, t);
   float acc = 0.f;
   for (int ks = 0; ks < p.nks; ++ks) {
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(D) void simt_dq_kernel(BwdParams bp) {
       float s = q * k, dp = dov * v;
       wg_sum2<D>(s, dp, red);
       const float pr = expf(p.scale * s - lse);
-      acc += pr * (dp - dl) * k;
+      acc += pr * (dp + ndl) * k;
     }
   }
   float* dst = bp.dq + qrow * D + d;
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(D) void simt_dkv_kernel(BwdParams bp) {
         float s = q * k, dp = dov * v;
         wg_sum2<D>(s, dp, red);
         const float pr = expf(p.scale * s - bp.lse[qrow]);
-        dk += pr * (dp - bp.delta[qrow]) * q;
+        dk += pr * (dp + bp.delta[qrow]) * q;  // the workspace holds -delta
         dv += pr * dov;
       }
     }

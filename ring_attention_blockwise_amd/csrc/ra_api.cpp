@@ -453,7 +453,7 @@ int check_backward_ptrs(const float* o, const void* dout, const float* dk_shards
 }
 
 // Everything ra_rank_backward enqueues once its arguments are checked:
-// delta = rowsum(dO * O) into `delta`, then per launched step the dQ and
+// -delta = -rowsum(dO * O) into `delta`, then per launched step the dQ and
 // dK/dV kernels.
 int run_backward(RankRing& ring, const float* o, const float* lse, const void* dout, float* dq, float* dk_shards,
                  float* dv_shards, float* delta, void* stream) {
