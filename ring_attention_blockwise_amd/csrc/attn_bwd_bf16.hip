@@ -19,16 +19,19 @@
 //     kernel: S^T = K Q^T and dP^T = V dO^T (K, V rows from LDS, Q^T and dO^T
 //     in registers), then dQ^T += K^T dS^T with K^T gathered by transposing
 //     LDS reads.
-//   * dK and dV, fused (the default): an eight-wave workgroup owns 128 keys
-//     of one (batch, kv head) and walks the query tiles (32 rows) of every
-//     query head of the group that see them.  Waves 0..3 (32 keys each, K^T
-//     and V^T in registers for the whole item) form S = Q K^T and dP = dO V^T
-//     and add dK^T += Q^T dS, and they leave each query tile's P, rounded to
-//     bf16, in LDS; waves 4..7 add dV^T += dO^T P one query tile behind, from
-//     that P and the tile's dO while it is still staged (three stages of Q,
-//     dO, L and P).  The dV waves recompute neither S nor P.  One wave holding
-//     both accumulators would need about 290 registers (one wave per SIMD);
-//     split over two waves of a SIMD they fit.
+//   * dK and dV in one launch (the default): an eight-wave workgroup owns
+//     128 keys of one (batch, kv head) and walks the query tiles (32 rows) of
+//     every query head of the group that see them; waves w and w + 4 share
+//     keys 32w .. 32w + 31, with K^T or V^T in registers for the whole item.
+//     The four products of a (query tile, key tile) pair on this side (the
+//     dQ kernel takes the other three) are split two and two between the two
+//     waves of a SIMD: waves 0..3 form S = Q K^T and P (P to LDS as bf16) and
+//     add dK^T += Q^T dS; waves 4..7 form dP - delta = dO V^T - delta (to LDS
+//     as float32) and add dV^T += dO^T P, each using the other group's result
+//     of the previous query tile, so the groups meet only at the one barrier
+//     per tile.  One wave holding both accumulators
+//     would need about 290 registers (one wave per SIMD); split over two
+//     waves of a SIMD they fit.
 //   * dV and dK, separate (two kernels of one template), for launches whose
 //     key tiles would not give every CU a workgroup: the same walk, S formed
 //     in both; eight-wave workgroups let two groups of four waves share a key
@@ -483,13 +486,11 @@ struct KvState {
 
 // Tile t of the list from buffers CUR while tile t+1 is copied into NXT;
 // te: end of this wave group's part of the list (tiles at or past it only
-// keep the group in step with the other at the barrier).  kPOut (dK only):
-// also leave the tile's P, rounded to bf16, at pout (2 KB per wave).
-template <int CUR, int NXT, bool kDK, bool kExt, bool kPOut = false>
+// keep the group in step with the other at the barrier).
+template <int CUR, int NXT, bool kDK, bool kExt>
 __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPlan& qp, const KvItem& it,
                                const KvStage& stg, QCursor& cur, int t, int te, RA_LDS char* const* qbuf,
-                               RA_LDS char* const* dbuf, RA_LDS char* const* lbuf, unsigned lane, int wave,
-                               RA_LDS char* pout = nullptr) {
+                               RA_LDS char* const* dbuf, RA_LDS char* const* lbuf, unsigned lane, int wave) {
   const StepParams& p = bp.s;
   const QCursor ci = cur;
   if (t + 1 < te) {
@@ -560,7 +561,7 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
 #pragma unroll
         for (int e = 0; e < 4; ++e) lo[e] = a0[e], lo[e + 4] = a1[e], hi[e] = c0[e], hi[e + 4] = c1[e];
       }
-      f32x8 x, xp;
+      f32x8 x;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // No guard for rows past the tile's end: their Q, dO, L and delta
@@ -572,11 +573,7 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
         if (kExt) a = (lo[e] <= dk && dk <= hi[e]) ? a : kNegInf;
         const float pr = __builtin_amdgcn_exp2f(a);
         x[e] = kDK ? pr * dp[8 * hf + e] : pr;
-        if (kPOut) xp[e] = pr;
       }
-      // P as the dV product takes it (the fused kernel's other wave group)
-      if (kPOut)
-        *(RA_LDS bf16x8*)(pout + (wave * 2 + hf) * 1024 + lane * 16) = __builtin_convertvector(xp, bf16x8);
       const bf16x8 xb = __builtin_convertvector(x, bf16x8);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -740,17 +737,305 @@ void attn_bwd_kv_kernel(BwdParams bp) {
     }
 }
 
-// dK and dV in one launch: eight waves per key tile of 128 keys.  Waves 0..3
-// run the dK tile above and also leave each query tile's P (bf16, exactly the
-// operand the dV product takes) in LDS; waves 4..7 add dV^T += dO^T P one
-// query tile behind, from that P and the tile's dO while it is still staged.
-// Three stages of Q, dO, L and P keep tile t+1's copy off tile t-1.  The dV
-// waves recompute neither S nor P: the pair issues 32 products per query
-// tile where the two separate kernels issue 40.  Used when the query tiles
-// are not split between wave groups (every CU gets key tiles).
+// ===========================================================================
+// dK and dV in one launch with the products split evenly between the two
+// wave groups of a key tile (128 keys; waves w and w + 4 share keys 32w ..
+// 32w + 31).  Iteration t of the query-tile list:
+//   dK waves: S(t) = Q K^T, P(t) = exp2(S sl2 - L log2 e), P(t) to LDS as
+//     bf16 (the dV product's operand) and kept in float32 registers; then,
+//     for tile t - 1, dS = P (dP - delta) with dP - delta from the dV waves,
+//     and dK^T += Q^T dS.
+//   dV waves: dP(t) - delta = dO V^T - delta (the product chain starts from
+//     the staged -delta), to LDS as float32; then, for tile t - 1, dV^T +=
+//     dO^T P with P from the dK waves.
+// Each group stages its own operands of tile t + 1 (Q and L, or dO and
+// -delta); one barrier ends every iteration, so nothing inside an iteration
+// waits for the other group, and each SIMD runs one wave of each with 16
+// products apiece.  Q, dO, L and -delta are staged in three stages (tile t
+// is read in iterations t and t + 1), P and dP - delta in two.
+
+// Copy through the buffer unit into LDS at dst + 4 kBytes * lane (kBytes 16
+// or 4 per lane, lane offset voff into a record of nrec bytes at base), issued
+// from inline assembly so that the compiler does not see an LDS write in
+// flight: it cannot tell this kernel's staged buffers apart from the ones its
+// waves are reading and would otherwise wait for every copy before those
+// reads.  The kernel's own wait before each barrier covers the copies.  M0
+// carries the LDS address and is restored before the block ends; the copy
+// writes no register.  The resource words may come from v_readfirstlane, and a
+// buffer instruction reading an SGPR that a vector instruction wrote needs
+// five wait states, which the compiler does not insert for operands of inline
+// assembly: the two moves and s_nop 2 give them.
+template <int kBytes>
+__device__ inline void kvb_copy(const void* base, int nrec, unsigned voff, RA_LDS void* dst) {
+  const unsigned long long a = (unsigned long long)base;
+  u32x4 r;
+  r[0] = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  r[1] = (unsigned)__builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xffffu));
+  r[2] = (unsigned)__builtin_amdgcn_readfirstlane(nrec);
+  r[3] = (unsigned)kRsrcWord3;
+  const int m = __builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)dst);
+  int saved;
+  if constexpr (kBytes == 16)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 2\n\tbuffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(m), "s"(r)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 2\n\tbuffer_load_dword %1, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(m), "s"(r)
+        : "memory");
+}
+
+struct KvbStage {
+  const char* xbase;     // row 0 of (batch b, query head 0) in Q (dK group) or dO (dV group)
+  const float* sbase;    // (b, row 0, head 0) in L (dK group) or in -delta (dV group)
+  unsigned row_bytes;    // Hq * 2D
+  unsigned off[2];
+  int wave, Hq;
+
+  __device__ void init(const BwdParams& bp, const KvItem& it, int w, unsigned lane, bool dv) {
+    const StepParams& p = bp.s;
+    Hq = p.Hq;
+    row_bytes = (unsigned)(p.Hq * kRowB);
+    const long long base = (long long)it.b * p.Sq * p.Hq;
+    xbase = (const char*)(dv ? bp.dout : p.q) + base * kRowB;
+    sbase = (dv ? bp.delta : bp.lse) + base;
+    wave = w;
+    off[0] = dma_off(w, 0, lane, row_bytes);
+    off[1] = dma_off(w, 1, lane, row_bytes);
+  }
+  // Query tile `c` of head h: 32 rows of the group's tensor, and (wave 0) the
+  // rows' L at ldst[0, 256) or -delta at ldst[256, 512); with masks the dK
+  // group's waves 2 and 3 also write the rows' key ranges at ldst[512, 768).
+  // Rows past the tile's end read 0.
+  template <bool kExt, bool kDV>
+  __device__ void issue(const StepParams& p, const QCursor& c, int g, unsigned lane, RA_LDS char* xdst,
+                        RA_LDS char* ldst) const {
+    const int h = g * p.G + c.hh;
+    const long long qin = (long long)c.tile * 32;
+    const long long local0 = (c.span ? p.qs_off[1] : p.qs_off[0]) + qin;
+    const int count = (int)min(32LL, (c.span ? p.qs_len[1] : p.qs_len[0]) - qin);
+    const long long o = local0 * (long long)row_bytes + (long long)h * kRowB;
+    const int nrec = (count - 1) * (int)row_bytes + kRowB;
+    // the key ranges first: with packed sequences they are looked up in
+    // global memory, and the wait for that lookup then covers no copy of
+    // this tile
+    if (kExt && !kDV && wave >= 2 && lane < 32) {
+      const long long qg = (c.span ? p.qs_start[1] : p.qs_start[0]) + (long long)c.tile * 32;
+      const long long v = wave == 2 ? key_lo(p, qg + lane) : key_hi(p, qg + lane);
+      ((RA_LDS int*)(ldst + 512))[(wave - 2) * 32 + lane] = (int)max(-(1LL << 30), min(1LL << 30, v - qg));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) kvb_copy<16>(xbase + o, nrec, off[i], xdst + (wave * 2 + i) * 1024);
+    if (wave == 0) {
+      const float* src = sbase + local0 * Hq + h;
+      const int nr = ((count - 1) * Hq + 1) * 4;
+      kvb_copy<4>(src, nr, lane * (unsigned)Hq * 4u, ldst + (kDV ? 256 : 0));
+    }
+  }
+};
+
+// The end of the prologue: the K^T or V^T operand registers and tile 0
+// complete, then the barrier.  The wait is the compiler's own instruction, so
+// it knows that the operand loads complete here and adds no wait for them
+// inside the loop, where it would also wait for the copies in flight.
+__device__ inline void kvb_begin() {
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Whether the wave's 32 keys meet query tile c at all (causal: its first key
+// at or before the tile's last row).
+__device__ inline bool kvb_live(const StepParams& p, const QCursor& c, long long kwg, bool has_keys) {
+  const long long qin = (long long)c.tile * 32;
+  const long long qglob = (c.span ? p.qs_start[1] : p.qs_start[0]) + qin;
+  const int qcount = (int)min(32LL, (c.span ? p.qs_len[1] : p.qs_len[0]) - qin);
+  return has_keys && (!p.causal || kwg <= qglob + qcount - 1);
+}
+
+struct KvbDk {
+  bf16x8 k[kD / 16];      // K^T operand: K[key l%32][16u + 8(l/32) .. +7]
+  f32x16 acc[kD / 32];    // dK^T accumulators
+  f32x16 pk;              // P of the previous tile, float32
+  bool live_prev;
+};
+
+// Iteration t of the dK group; T6 = t mod 6 names the stages statically.
+template <int T6, bool kExt>
+__device__ inline void kvb_dk_iter(KvbDk& st, const BwdParams& bp, const QPlan& qp, const KvItem& it,
+                                   const KvbStage& stg, QCursor& cur, int t, int n, RA_LDS char* const* qbuf,
+                                   RA_LDS char* const* lbuf, RA_LDS char* const* pbuf, RA_LDS char* const* gbuf,
+                                   unsigned lane, int wave, long long kwg, bool has_keys) {
+  constexpr int CUR = T6 % 3, PRV = (T6 + 2) % 3, NXT = (T6 + 1) % 3, PC = T6 % 2, PP = (T6 + 1) % 2;
+  const StepParams& p = bp.s;
+  const QCursor ci = cur;
+  if (t + 1 < n) {
+    cur.advance(qp);
+    stg.template issue<kExt, false>(p, cur, it.g, lane, qbuf[NXT], lbuf[NXT]);
+  }
+  const int L = (int)(lane >> 5);
+  bool live = false;
+  f32x16 pk = f32x16{};
+  if (t < n) {
+    live = kvb_live(p, ci, kwg, has_keys);
+    if (live) {
+      const unsigned rb = row_base_sigma(lane);
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int u = 0; u < kD / 16; ++u) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(qbuf[CUR], rb ^ (32u * u)));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.k[u], s, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // rows of register r: 16(r/8) + 8L + r%8 of the tile; the lane's key
+      const int key = (int)(lane & 31u);
+      const long long qglob = (ci.span ? p.qs_start[1] : p.qs_start[0]) + (long long)ci.tile * 32;
+      const RA_LDS int* rt = (const RA_LDS int*)(lbuf[CUR] + 512);
+      const int dk = kExt ? (int)max(-(1LL << 30), min(1LL << 30, kwg - qglob)) + key : 0;
+      if (!kExt && p.causal && kwg + 31 > qglob) {
+        // row i sees key j iff qglob + i >= kwg + j
+        const int dd = (int)max(-1024LL, min(1024LL, qglob - kwg)) + 8 * L - key;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = neg_inf_select(dd + 16 * (r >> 3) + (r & 7), s[r]);
+      }
+      const RA_LDS float* lt = (const RA_LDS float*)lbuf[CUR];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 l0 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L);
+        const f32x4 l1 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L + 4);
+        const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+        int lo[8], hi[8];
+        if (kExt) {
+          const i32x4 a0 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L);
+          const i32x4 a1 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L + 4);
+          const i32x4 c0 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L);
+          const i32x4 c1 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lo[e] = a0[e], lo[e + 4] = a1[e], hi[e] = c0[e], hi[e + 4] = c1[e];
+        }
+        f32x8 xp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // rows past the tile's end were staged as zeros (P = 1 times zero
+          // rows); L is finite on every real row; a key outside the row's
+          // range gets exponent -inf (a select before exp2)
+          float a = __builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e);
+          if (kExt) a = (lo[e] <= dk && dk <= hi[e]) ? a : kNegInf;
+          xp[e] = __builtin_amdgcn_exp2f(a);
+          pk[8 * hf + e] = xp[e];
+        }
+        *(RA_LDS bf16x8*)(pbuf[PC] + (wave * 2 + hf) * 1024 + lane * 16) = __builtin_convertvector(xp, bf16x8);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (t > 0 && st.live_prev) {
+    // dS of tile t - 1 from its P (kept) and dP - delta (the dV waves'),
+    // then dK^T += Q^T dS over its two 16-row halves
+    const RA_LDS f32x4* g = (const RA_LDS f32x4*)(gbuf[PP] + wave * 4096) + lane;
+    unsigned b0, b1;
+    tr_bases(lane, b0, b1);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 g0 = g[(2 * hf) * 64], g1 = g[(2 * hf + 1) * 64];
+      f32x8 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = st.pk[8 * hf + e] * g0[e];
+        x[e + 4] = st.pk[8 * hf + 4 + e] * g1[e];
+      }
+      const bf16x8 xb = __builtin_convertvector(x, bf16x8);
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db) {
+        const unsigned o0 = (b0 ^ (64u * db)) + 16u * kRowB * hf, o1 = (b1 ^ (64u * db)) + 16u * kRowB * hf;
+        st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qbuf[PRV], o0, o1), xb, st.acc[db], 0, 0, 0);
+      }
+    }
+  }
+  st.pk = pk;
+  st.live_prev = live;
+  if (t < n) {
+    wait_loads();
+    __syncthreads();
+  }
+}
+
+struct KvbDv {
+  bf16x8 v[kD / 16];      // V^T operand, the layout of K^T in KvbDk
+  f32x16 acc[kD / 32];    // dV^T accumulators
+  bool live_prev;
+};
+
+template <int T6, bool kExt>
+__device__ inline void kvb_dv_iter(KvbDv& st, const BwdParams& bp, const QPlan& qp, const KvItem& it,
+                                   const KvbStage& stg, QCursor& cur, int t, int n, RA_LDS char* const* dbuf,
+                                   RA_LDS char* const* lbuf, RA_LDS char* const* pbuf, RA_LDS char* const* gbuf,
+                                   unsigned lane, int wave, long long kwg, bool has_keys) {
+  constexpr int CUR = T6 % 3, PRV = (T6 + 2) % 3, NXT = (T6 + 1) % 3, PC = T6 % 2, PP = (T6 + 1) % 2;
+  const StepParams& p = bp.s;
+  const QCursor ci = cur;
+  if (t + 1 < n) {
+    cur.advance(qp);
+    stg.template issue<kExt, true>(p, cur, it.g, lane, dbuf[NXT], lbuf[NXT]);
+  }
+  bool live = false;
+  if (t < n) {
+    live = kvb_live(p, ci, kwg, has_keys);
+    if (live) {
+      // dP - delta: the chain starts from the rows' -delta (register r of the
+      // lane is row 16(r/8) + 8L + r%8)
+      const int L = (int)(lane >> 5);
+      const RA_LDS float* lt = (const RA_LDS float*)lbuf[CUR];
+      f32x16 dp;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 t0 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L);
+        const f32x4 t1 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[8 * hf + e] = t0[e], dp[8 * hf + 4 + e] = t1[e];
+      }
+      const unsigned rb = row_base_sigma(lane);
+#pragma unroll
+      for (int u = 0; u < kD / 16; ++u) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, lds_load16(dbuf[CUR], rb ^ (32u * u)));
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, st.v[u], dp, 0, 0, 0);
+      }
+      RA_LDS f32x4* g = (RA_LDS f32x4*)(gbuf[PC] + wave * 4096) + lane;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) g[k * 64] = f32x4{dp[4 * k], dp[4 * k + 1], dp[4 * k + 2], dp[4 * k + 3]};
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (t > 0 && st.live_prev) {
+    // dV^T += dO^T P for tile t - 1, P from the dK waves
+    unsigned b0, b1;
+    tr_bases(lane, b0, b1);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const bf16x8 xb = *(const RA_LDS bf16x8*)(pbuf[PP] + (wave * 2 + hf) * 1024 + lane * 16);
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db) {
+        const unsigned o0 = (b0 ^ (64u * db)) + 16u * kRowB * hf, o1 = (b1 ^ (64u * db)) + 16u * kRowB * hf;
+        st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(dbuf[PRV], o0, o1), xb, st.acc[db], 0, 0, 0);
+      }
+    }
+  }
+  st.live_prev = live;
+  if (t < n) {
+    wait_loads();
+    __syncthreads();
+  }
+}
+
 template <bool kExt>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_bwd_kvf_kernel(BwdParams bp) {
+void attn_bwd_kvb_kernel(BwdParams bp) {
   const StepParams& p = bp.s;
   __shared__ __attribute__((aligned(16))) char q0_raw[kTileB];
   __shared__ __attribute__((aligned(16))) char q1_raw[kTileB];
@@ -758,12 +1043,16 @@ void attn_bwd_kvf_kernel(BwdParams bp) {
   __shared__ __attribute__((aligned(16))) char d0_raw[kTileB];
   __shared__ __attribute__((aligned(16))) char d1_raw[kTileB];
   __shared__ __attribute__((aligned(16))) char d2_raw[kTileB];
-  __shared__ __attribute__((aligned(16))) char l0_raw[768];
+  __shared__ __attribute__((aligned(16))) char l0_raw[768];  // L, -delta, and with masks the rows' key ranges
   __shared__ __attribute__((aligned(16))) char l1_raw[768];
   __shared__ __attribute__((aligned(16))) char l2_raw[768];
-  __shared__ __attribute__((aligned(16))) char p0_raw[kTileB];  // 4 waves x 2 halves x 1 KB
+  __shared__ __attribute__((aligned(16))) char p0_raw[kTileB];      // P: 4 waves x 2 halves x 1 KB
   __shared__ __attribute__((aligned(16))) char p1_raw[kTileB];
-  __shared__ __attribute__((aligned(16))) char p2_raw[kTileB];
+  __shared__ __attribute__((aligned(16))) char g0_raw[4 * 4096];    // dP - delta: 4 waves x 4 KB
+  __shared__ __attribute__((aligned(16))) char g1_raw[4 * 4096];
+  RA_LDS char* const lbuf[3] = {(RA_LDS char*)l0_raw, (RA_LDS char*)l1_raw, (RA_LDS char*)l2_raw};
+  RA_LDS char* const pbuf[2] = {(RA_LDS char*)p0_raw, (RA_LDS char*)p1_raw};
+  RA_LDS char* const gbuf[2] = {(RA_LDS char*)g0_raw, (RA_LDS char*)g1_raw};
   const unsigned lane = threadIdx.x & 63u;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wave = wv & 3;  // the wave's 32 keys within the tile
@@ -776,53 +1065,49 @@ void attn_bwd_kvf_kernel(BwdParams bp) {
   const int key = 32 * wave + (int)(lane & 31u);
   const long long krow = ((long long)it.b * p.Sk + it.klocal0 + key) * p.Hkv + it.g;
   const int dsub = 4 * (int)(lane >> 5);
+  const long long kwg = it.kglob0 + 32 * wave;
+  const bool has_keys = 32 * wave < it.kcount;
+  const bool kok = key < it.kcount;
+  const long long ro = ((long long)it.b * p.Sk * p.Hkv + it.g) * (long long)kRowB +
+                       (it.klocal0 + key) * (long long)(p.Hkv * kRowB);
+  const bool dv = wv >= 4;
+  KvbStage stg;
+  stg.init(bp, it, wave, lane, dv);
+  QCursor cur;
+  cur.first(qp);
 
-  if (wv < 4) {
-    // the dK waves carry the chain of each tile (products, exponentials,
-    // products); the dV waves' products fill its gaps (measured +0.6%, and
-    // -2.6% the other way round)
-    __builtin_amdgcn_s_setprio(1);
+  if (!dv) {
     RA_LDS char* const qbuf[3] = {(RA_LDS char*)q0_raw, (RA_LDS char*)q1_raw, (RA_LDS char*)q2_raw};
-    RA_LDS char* const dbuf[3] = {(RA_LDS char*)d0_raw, (RA_LDS char*)d1_raw, (RA_LDS char*)d2_raw};
-    RA_LDS char* const lbuf[3] = {(RA_LDS char*)l0_raw, (RA_LDS char*)l1_raw, (RA_LDS char*)l2_raw};
-    KvState<true> st;
-    {
-      const bool kok = key < it.kcount;
-      const long long ro = ((long long)it.b * p.Sk * p.Hkv + it.g) * (long long)kRowB +
-                           (it.klocal0 + key) * (long long)(p.Hkv * kRowB);
-      const uint16_t* kr = (const uint16_t*)((const char*)p.k + ro);
-      const uint16_t* vr = (const uint16_t*)((const char*)p.v + ro);
+    KvbDk st;
+    const uint16_t* kr = (const uint16_t*)((const char*)p.k + ro);
 #pragma unroll
-      for (int u = 0; u < kD / 16; ++u) {
-        st.k[u] = kok ? *(const bf16x8*)(kr + 16 * u + 8 * (lane >> 5)) : bf16x8{};
-        st.v[u] = kok ? *(const bf16x8*)(vr + 16 * u + 8 * (lane >> 5)) : bf16x8{};
-      }
+    for (int u = 0; u < kD / 16; ++u) st.k[u] = kok ? *(const bf16x8*)(kr + 16 * u + 8 * (lane >> 5)) : bf16x8{};
 #pragma unroll
-      for (int db = 0; db < kD / 32; ++db) st.acc[db] = f32x16{};
-    }
-    KvStage stg;
-    stg.init(bp, it, wave, lane);
-    QCursor cur;
-    cur.first(qp);
-    stg.template issue<kExt>(p, qp, cur, it.g, lane, qbuf[0], dbuf[0], lbuf[0]);
-    wait_loads();
-    __syncthreads();
+    for (int db = 0; db < kD / 32; ++db) st.acc[db] = f32x16{};
+    st.pk = f32x16{};
+    st.live_prev = false;
+    stg.template issue<kExt, false>(p, cur, it.g, lane, qbuf[0], lbuf[0]);
+    kvb_begin();
     int t = 0;
-    for (; t + 2 < n; t += 3) {
-      kv_tile<0, 1, true, kExt, true>(st, bp, qp, it, stg, cur, t, n, qbuf, dbuf, lbuf, lane, wave,
-                                      (RA_LDS char*)p0_raw);
-      kv_tile<1, 2, true, kExt, true>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, dbuf, lbuf, lane, wave,
-                                      (RA_LDS char*)p1_raw);
-      kv_tile<2, 0, true, kExt, true>(st, bp, qp, it, stg, cur, t + 2, n, qbuf, dbuf, lbuf, lane, wave,
-                                      (RA_LDS char*)p2_raw);
+    for (; t + 5 <= n; t += 6) {
+      kvb_dk_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<5, kExt>(st, bp, qp, it, stg, cur, t + 5, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
     }
-    if (t < n)
-      kv_tile<0, 1, true, kExt, true>(st, bp, qp, it, stg, cur, t, n, qbuf, dbuf, lbuf, lane, wave,
-                                      (RA_LDS char*)p0_raw);
-    if (t + 1 < n)
-      kv_tile<1, 2, true, kExt, true>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, dbuf, lbuf, lane, wave,
-                                      (RA_LDS char*)p1_raw);
-    if (key >= it.kcount) return;
+    // the rest of t = 0 .. n (at most six iterations, the last one t = n)
+    if (t <= n) kvb_dk_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    if (t + 1 <= n)
+      kvb_dk_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    if (t + 2 <= n)
+      kvb_dk_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    if (t + 3 <= n)
+      kvb_dk_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    if (t + 4 <= n)
+      kvb_dk_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    if (!kok) return;
     float* dst = bp.dk + krow * kD;
 #pragma unroll
     for (int db = 0; db < kD / 32; ++db)
@@ -839,45 +1124,35 @@ void attn_bwd_kvf_kernel(BwdParams bp) {
     return;
   }
 
-  // dV waves: query tile t-1 during the dK waves' tile t (stage (t-1) mod 3)
-  f32x16 acc[kD / 32];
+  RA_LDS char* const dbuf[3] = {(RA_LDS char*)d0_raw, (RA_LDS char*)d1_raw, (RA_LDS char*)d2_raw};
+  KvbDv st;
+  const uint16_t* vr = (const uint16_t*)((const char*)p.v + ro);
 #pragma unroll
-  for (int db = 0; db < kD / 32; ++db) acc[db] = f32x16{};
-  unsigned b0, b1;
-  tr_bases(lane, b0, b1);
-  QCursor cur;  // tile t-1
-  cur.first(qp);
-  const long long kwg = it.kglob0 + 32 * wave;
-  const bool has_keys = 32 * wave < it.kcount;
-  __syncthreads();  // the dK waves' first tile is staged
-  for (int t = 0; t <= n; ++t) {
-    if (t > 0) {
-      // the dK waves wrote P of this tile only where they had work (the same
-      // test as theirs)
-      const long long qin = (long long)cur.tile * 32;
-      const long long qglob = (cur.span ? p.qs_start[1] : p.qs_start[0]) + qin;
-      const int qcount = (int)min(32LL, (cur.span ? p.qs_len[1] : p.qs_len[0]) - qin);
-      const bool live = has_keys && (!p.causal || kwg <= qglob + qcount - 1);
-      const int ix = (t - 1) % 3;
-      RA_LDS char* const dt = ix == 0 ? (RA_LDS char*)d0_raw : ix == 1 ? (RA_LDS char*)d1_raw : (RA_LDS char*)d2_raw;
-      RA_LDS char* const pt = ix == 0 ? (RA_LDS char*)p0_raw : ix == 1 ? (RA_LDS char*)p1_raw : (RA_LDS char*)p2_raw;
-      if (live) {
+  for (int u = 0; u < kD / 16; ++u) st.v[u] = kok ? *(const bf16x8*)(vr + 16 * u + 8 * (lane >> 5)) : bf16x8{};
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const bf16x8 xb = *(const RA_LDS bf16x8*)(pt + (wave * 2 + hf) * 1024 + lane * 16);
-#pragma unroll
-          for (int db = 0; db < kD / 32; ++db) {
-            const unsigned o0 = (b0 ^ (64u * db)) + 16u * kRowB * hf, o1 = (b1 ^ (64u * db)) + 16u * kRowB * hf;
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(dt, o0, o1), xb, acc[db], 0, 0, 0);
-          }
-        }
-      }
-      cur.advance(qp);
-    }
-    // one barrier per dK tile; none after the last (nothing is staged then)
-    if (t < n) __syncthreads();
+  for (int db = 0; db < kD / 32; ++db) st.acc[db] = f32x16{};
+  st.live_prev = false;
+  stg.template issue<kExt, true>(p, cur, it.g, lane, dbuf[0], lbuf[0]);
+  kvb_begin();
+  int t = 0;
+  for (; t + 5 <= n; t += 6) {
+    kvb_dv_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<5, kExt>(st, bp, qp, it, stg, cur, t + 5, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
   }
-  if (key >= it.kcount) return;
+  if (t <= n) kvb_dv_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+  if (t + 1 <= n)
+    kvb_dv_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+  if (t + 2 <= n)
+    kvb_dv_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+  if (t + 3 <= n)
+    kvb_dv_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+  if (t + 4 <= n)
+    kvb_dv_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+  if (!kok) return;
   float* dst = bp.dv + krow * kD;
 #pragma unroll
   for (int db = 0; db < kD / 32; ++db)
@@ -885,10 +1160,10 @@ void attn_bwd_kvf_kernel(BwdParams bp) {
     for (int j = 0; j < 4; ++j) {
       const int c = 32 * db + 8 * j + dsub;
       float4 r = *(const float4*)(dst + c);
-      r.x += acc[db][4 * j];
-      r.y += acc[db][4 * j + 1];
-      r.z += acc[db][4 * j + 2];
-      r.w += acc[db][4 * j + 3];
+      r.x += st.acc[db][4 * j];
+      r.y += st.acc[db][4 * j + 1];
+      r.z += st.acc[db][4 * j + 2];
+      r.w += st.acc[db][4 * j + 3];
       *(float4*)(dst + c) = r;
     }
 }
@@ -945,12 +1220,12 @@ hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s) {
       hipLaunchKernelGGL((attn_bwd_kv_kernel<false, true, true>), grid, blk, 0, s, p);
       hipLaunchKernelGGL((attn_bwd_kv_kernel<true, true, true>), grid, blk, 0, s, p);
     } else if (ext) {
-      hipLaunchKernelGGL(attn_bwd_kvf_kernel<true>, grid, blk, 0, s, p);
+      hipLaunchKernelGGL(attn_bwd_kvb_kernel<true>, grid, blk, 0, s, p);
     } else if (p.kv_split) {
       hipLaunchKernelGGL((attn_bwd_kv_kernel<false, false, true>), grid, blk, 0, s, p);
       hipLaunchKernelGGL((attn_bwd_kv_kernel<true, false, true>), grid, blk, 0, s, p);
     } else {
-      hipLaunchKernelGGL(attn_bwd_kvf_kernel<false>, grid, blk, 0, s, p);
+      hipLaunchKernelGGL(attn_bwd_kvb_kernel<false>, grid, blk, 0, s, p);
     }
   }
   return hipGetLastError();
