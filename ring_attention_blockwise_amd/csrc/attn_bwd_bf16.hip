@@ -791,6 +791,65 @@ __device__ inline void kvb_copy(const void* base, int nrec, unsigned voff, RA_LD
         : "memory");
 }
 
+// The query tile list of a key tile (heads outer, then spans, then tiles),
+// with what staging and masking take of the current tile carried from tile to
+// tile by additions; only a move to the other span or the next head goes back
+// to the plan.  Q and dO share a layout, and so do L and -delta, so the one
+// cursor serves both wave groups.
+struct KvbCursor {
+  int hh, span, tile;
+  int left;          // rows of the span from the tile's first row on
+  int qrel;          // qglob - kwg (the wave's first key), held in [-2^30, 2^30]
+  long long xoff;    // bytes from (b, row 0, head 0) to the tile's first row, head h, in Q or dO
+  long long soff;    // floats from (b, row 0, head 0) to the same row in L or -delta
+  long long qglob;   // global position of the tile's first row
+  long long kwg;
+
+  __device__ int count() const { return min(32, left); }
+  __device__ void place(const StepParams& p, int g, unsigned row_bytes) {
+    const long long qin = (long long)tile * 32;
+    const long long local0 = (span ? p.qs_off[1] : p.qs_off[0]) + qin;
+    const int h = g * p.G + hh;
+    left = (int)((span ? p.qs_len[1] : p.qs_len[0]) - qin);
+    xoff = local0 * row_bytes + (long long)h * kRowB;
+    soff = local0 * p.Hq + h;
+    qglob = (span ? p.qs_start[1] : p.qs_start[0]) + qin;
+    qrel = (int)max(-(1LL << 30), min(1LL << 30, qglob - kwg));
+  }
+  __device__ void first(const StepParams& p, const QPlan& qp, int g, unsigned row_bytes, long long kwg_) {
+    kwg = kwg_;
+    hh = 0;
+    span = qp.tend[0] > qp.tbeg[0] ? 0 : 1;
+    tile = span ? qp.tbeg[1] : qp.tbeg[0];
+    place(p, g, row_bytes);
+  }
+  __device__ void advance(const StepParams& p, const QPlan& qp, int g, unsigned row_bytes) {
+    ++tile;
+    if (tile < (span ? qp.tend[1] : qp.tend[0])) {
+      left -= 32;
+      xoff += 32LL * row_bytes;
+      soff += 32LL * p.Hq;
+      qglob += 32;
+      // exact while above -2^29 (a value held at 2^30 stays there: the rows
+      // only move on); below, from the positions again
+      if (qrel > -(1 << 29))
+        qrel = min(qrel + 32, 1 << 30);
+      else
+        qrel = (int)max(-(1LL << 30), min(1LL << 30, qglob - kwg));
+      return;
+    }
+    if (span == 0 && qp.tend[1] > qp.tbeg[1]) {
+      span = 1;
+      tile = qp.tbeg[1];
+    } else {
+      ++hh;
+      span = qp.tend[0] > qp.tbeg[0] ? 0 : 1;
+      tile = span ? qp.tbeg[1] : qp.tbeg[0];
+    }
+    place(p, g, row_bytes);
+  }
+};
+
 struct KvbStage {
   const char* xbase;     // row 0 of (batch b, query head 0) in Q (dK group) or dO (dV group)
   const float* sbase;    // (b, row 0, head 0) in L (dK group) or in -delta (dV group)
@@ -809,31 +868,26 @@ struct KvbStage {
     off[0] = dma_off(w, 0, lane, row_bytes);
     off[1] = dma_off(w, 1, lane, row_bytes);
   }
-  // Query tile `c` of head h: 32 rows of the group's tensor, and (wave 0) the
-  // rows' L at ldst[0, 256) or -delta at ldst[256, 512); with masks the dK
-  // group's waves 2 and 3 also write the rows' key ranges at ldst[512, 768).
-  // Rows past the tile's end read 0.
+  // Query tile c: 32 rows of the group's tensor, and (wave 0) the rows' L at
+  // ldst[0, 256) or -delta at ldst[256, 512); with masks the dK group's waves
+  // 2 and 3 also write the rows' key ranges at ldst[512, 768).  Rows past the
+  // tile's end read 0.
   template <bool kExt, bool kDV>
-  __device__ void issue(const StepParams& p, const QCursor& c, int g, unsigned lane, RA_LDS char* xdst,
+  __device__ void issue(const StepParams& p, const KvbCursor& c, unsigned lane, RA_LDS char* xdst,
                         RA_LDS char* ldst) const {
-    const int h = g * p.G + c.hh;
-    const long long qin = (long long)c.tile * 32;
-    const long long local0 = (c.span ? p.qs_off[1] : p.qs_off[0]) + qin;
-    const int count = (int)min(32LL, (c.span ? p.qs_len[1] : p.qs_len[0]) - qin);
-    const long long o = local0 * (long long)row_bytes + (long long)h * kRowB;
+    const int count = c.count();
     const int nrec = (count - 1) * (int)row_bytes + kRowB;
     // the key ranges first: with packed sequences they are looked up in
     // global memory, and the wait for that lookup then covers no copy of
     // this tile
     if (kExt && !kDV && wave >= 2 && lane < 32) {
-      const long long qg = (c.span ? p.qs_start[1] : p.qs_start[0]) + (long long)c.tile * 32;
-      const long long v = wave == 2 ? key_lo(p, qg + lane) : key_hi(p, qg + lane);
-      ((RA_LDS int*)(ldst + 512))[(wave - 2) * 32 + lane] = (int)max(-(1LL << 30), min(1LL << 30, v - qg));
+      const long long v = wave == 2 ? key_lo(p, c.qglob + lane) : key_hi(p, c.qglob + lane);
+      ((RA_LDS int*)(ldst + 512))[(wave - 2) * 32 + lane] = (int)max(-(1LL << 30), min(1LL << 30, v - c.qglob));
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) kvb_copy<16>(xbase + o, nrec, off[i], xdst + (wave * 2 + i) * 1024);
+    for (int i = 0; i < 2; ++i) kvb_copy<16>(xbase + c.xoff, nrec, off[i], xdst + (wave * 2 + i) * 1024);
     if (wave == 0) {
-      const float* src = sbase + local0 * Hq + h;
+      const float* src = sbase + c.soff;
       const int nr = ((count - 1) * Hq + 1) * 4;
       kvb_copy<4>(src, nr, lane * (unsigned)Hq * 4u, ldst + (kDV ? 256 : 0));
     }
@@ -852,55 +906,54 @@ __device__ inline void kvb_begin() {
 
 // Whether the wave's 32 keys meet query tile c at all (causal: its first key
 // at or before the tile's last row).
-__device__ inline bool kvb_live(const StepParams& p, const QCursor& c, long long kwg, bool has_keys) {
-  const long long qin = (long long)c.tile * 32;
-  const long long qglob = (c.span ? p.qs_start[1] : p.qs_start[0]) + qin;
-  const int qcount = (int)min(32LL, (c.span ? p.qs_len[1] : p.qs_len[0]) - qin);
-  return has_keys && (!p.causal || kwg <= qglob + qcount - 1);
+__device__ inline bool kvb_live(const StepParams& p, const KvbCursor& c, bool has_keys) {
+  return has_keys && (!p.causal || c.qrel + c.count() - 1 >= 0);
 }
 
 struct KvbDk {
   bf16x8 k[kD / 16];      // K^T operand: K[key l%32][16u + 8(l/32) .. +7]
   f32x16 acc[kD / 32];    // dK^T accumulators
-  f32x16 pk;              // P of the previous tile, float32
+  f32x16 pk[2];           // P, float32, of the tiles of even and odd t
   bool live_prev;
 };
 
 // Iteration t of the dK group; T6 = t mod 6 names the stages statically.
 template <int T6, bool kExt>
 __device__ inline void kvb_dk_iter(KvbDk& st, const BwdParams& bp, const QPlan& qp, const KvItem& it,
-                                   const KvbStage& stg, QCursor& cur, int t, int n, RA_LDS char* const* qbuf,
+                                   const KvbStage& stg, KvbCursor& cur, int t, int n, RA_LDS char* const* qbuf,
                                    RA_LDS char* const* lbuf, RA_LDS char* const* pbuf, RA_LDS char* const* gbuf,
-                                   unsigned lane, int wave, long long kwg, bool has_keys) {
+                                   unsigned lane, int wave, bool has_keys) {
   constexpr int CUR = T6 % 3, PRV = (T6 + 2) % 3, NXT = (T6 + 1) % 3, PC = T6 % 2, PP = (T6 + 1) % 2;
   const StepParams& p = bp.s;
-  const QCursor ci = cur;
+  const KvbCursor ci = cur;
   if (t + 1 < n) {
-    cur.advance(qp);
-    stg.template issue<kExt, false>(p, cur, it.g, lane, qbuf[NXT], lbuf[NXT]);
+    cur.advance(p, qp, it.g, stg.row_bytes);
+    stg.template issue<kExt, false>(p, cur, lane, qbuf[NXT], lbuf[NXT]);
   }
   const int L = (int)(lane >> 5);
   bool live = false;
-  f32x16 pk = f32x16{};
+  f32x16& pk = st.pk[PC];  // tile t's P, read next iteration only if live
   if (t < n) {
-    live = kvb_live(p, ci, kwg, has_keys);
+    live = kvb_live(p, ci, has_keys);
     if (live) {
+      // every operand read issued before the product chain (the chain then
+      // waits only for the read it needs next)
       const unsigned rb = row_base_sigma(lane);
+      bf16x8 a[kD / 16];
+#pragma unroll
+      for (int u = 0; u < kD / 16; ++u) a[u] = __builtin_bit_cast(bf16x8, lds_load16(qbuf[CUR], rb ^ (32u * u)));
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 s = f32x16{};
 #pragma unroll
-      for (int u = 0; u < kD / 16; ++u) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(qbuf[CUR], rb ^ (32u * u)));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.k[u], s, 0, 0, 0);
-      }
+      for (int u = 0; u < kD / 16; ++u) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], st.k[u], s, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       // rows of register r: 16(r/8) + 8L + r%8 of the tile; the lane's key
       const int key = (int)(lane & 31u);
-      const long long qglob = (ci.span ? p.qs_start[1] : p.qs_start[0]) + (long long)ci.tile * 32;
       const RA_LDS int* rt = (const RA_LDS int*)(lbuf[CUR] + 512);
-      const int dk = kExt ? (int)max(-(1LL << 30), min(1LL << 30, kwg - qglob)) + key : 0;
-      if (!kExt && p.causal && kwg + 31 > qglob) {
+      const int dk = kExt ? key - ci.qrel : 0;
+      if (!kExt && p.causal && ci.qrel < 31) {
         // row i sees key j iff qglob + i >= kwg + j
-        const int dd = (int)max(-1024LL, min(1024LL, qglob - kwg)) + 8 * L - key;
+        const int dd = max(-1024, min(1024, ci.qrel)) + 8 * L - key;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = neg_inf_select(dd + 16 * (r >> 3) + (r & 7), s[r]);
       }
@@ -944,21 +997,23 @@ __device__ inline void kvb_dk_iter(KvbDk& st, const BwdParams& bp, const QPlan& 
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const f32x4 g0 = g[(2 * hf) * 64], g1 = g[(2 * hf + 1) * 64];
+      bf16x8 qt[kD / 32];
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db)
+        qt[db] = tr_read(qbuf[PRV], (b0 ^ (64u * db)) + 16u * kRowB * hf, (b1 ^ (64u * db)) + 16u * kRowB * hf);
+      __builtin_amdgcn_sched_barrier(0);
       f32x8 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[e] = st.pk[8 * hf + e] * g0[e];
-        x[e + 4] = st.pk[8 * hf + 4 + e] * g1[e];
+        x[e] = st.pk[PP][8 * hf + e] * g0[e];
+        x[e + 4] = st.pk[PP][8 * hf + 4 + e] * g1[e];
       }
       const bf16x8 xb = __builtin_convertvector(x, bf16x8);
 #pragma unroll
-      for (int db = 0; db < kD / 32; ++db) {
-        const unsigned o0 = (b0 ^ (64u * db)) + 16u * kRowB * hf, o1 = (b1 ^ (64u * db)) + 16u * kRowB * hf;
-        st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qbuf[PRV], o0, o1), xb, st.acc[db], 0, 0, 0);
-      }
+      for (int db = 0; db < kD / 32; ++db) st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[db], xb, st.acc[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  st.pk = pk;
   st.live_prev = live;
   if (t < n) {
     wait_loads();
@@ -974,19 +1029,19 @@ struct KvbDv {
 
 template <int T6, bool kExt>
 __device__ inline void kvb_dv_iter(KvbDv& st, const BwdParams& bp, const QPlan& qp, const KvItem& it,
-                                   const KvbStage& stg, QCursor& cur, int t, int n, RA_LDS char* const* dbuf,
+                                   const KvbStage& stg, KvbCursor& cur, int t, int n, RA_LDS char* const* dbuf,
                                    RA_LDS char* const* lbuf, RA_LDS char* const* pbuf, RA_LDS char* const* gbuf,
-                                   unsigned lane, int wave, long long kwg, bool has_keys) {
+                                   unsigned lane, int wave, bool has_keys) {
   constexpr int CUR = T6 % 3, PRV = (T6 + 2) % 3, NXT = (T6 + 1) % 3, PC = T6 % 2, PP = (T6 + 1) % 2;
   const StepParams& p = bp.s;
-  const QCursor ci = cur;
+  const KvbCursor ci = cur;
   if (t + 1 < n) {
-    cur.advance(qp);
-    stg.template issue<kExt, true>(p, cur, it.g, lane, dbuf[NXT], lbuf[NXT]);
+    cur.advance(p, qp, it.g, stg.row_bytes);
+    stg.template issue<kExt, true>(p, cur, lane, dbuf[NXT], lbuf[NXT]);
   }
   bool live = false;
   if (t < n) {
-    live = kvb_live(p, ci, kwg, has_keys);
+    live = kvb_live(p, ci, has_keys);
     if (live) {
       // dP - delta: the chain starts from the rows' -delta (register r of the
       // lane is row 16(r/8) + 8L + r%8)
@@ -1001,11 +1056,13 @@ __device__ inline void kvb_dv_iter(KvbDv& st, const BwdParams& bp, const QPlan& 
         for (int e = 0; e < 4; ++e) dp[8 * hf + e] = t0[e], dp[8 * hf + 4 + e] = t1[e];
       }
       const unsigned rb = row_base_sigma(lane);
+      bf16x8 b[kD / 16];
 #pragma unroll
-      for (int u = 0; u < kD / 16; ++u) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, lds_load16(dbuf[CUR], rb ^ (32u * u)));
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, st.v[u], dp, 0, 0, 0);
-      }
+      for (int u = 0; u < kD / 16; ++u) b[u] = __builtin_bit_cast(bf16x8, lds_load16(dbuf[CUR], rb ^ (32u * u)));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kD / 16; ++u) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[u], st.v[u], dp, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
       RA_LDS f32x4* g = (RA_LDS f32x4*)(gbuf[PC] + wave * 4096) + lane;
 #pragma unroll
       for (int k = 0; k < 4; ++k) g[k * 64] = f32x4{dp[4 * k], dp[4 * k + 1], dp[4 * k + 2], dp[4 * k + 3]};
@@ -1019,11 +1076,14 @@ __device__ inline void kvb_dv_iter(KvbDv& st, const BwdParams& bp, const QPlan& 
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const bf16x8 xb = *(const RA_LDS bf16x8*)(pbuf[PP] + (wave * 2 + hf) * 1024 + lane * 16);
+      bf16x8 dt[kD / 32];
 #pragma unroll
-      for (int db = 0; db < kD / 32; ++db) {
-        const unsigned o0 = (b0 ^ (64u * db)) + 16u * kRowB * hf, o1 = (b1 ^ (64u * db)) + 16u * kRowB * hf;
-        st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(dbuf[PRV], o0, o1), xb, st.acc[db], 0, 0, 0);
-      }
+      for (int db = 0; db < kD / 32; ++db)
+        dt[db] = tr_read(dbuf[PRV], (b0 ^ (64u * db)) + 16u * kRowB * hf, (b1 ^ (64u * db)) + 16u * kRowB * hf);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db) st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt[db], xb, st.acc[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   st.live_prev = live;
@@ -1073,8 +1133,8 @@ void attn_bwd_kvb_kernel(BwdParams bp) {
   const bool dv = wv >= 4;
   KvbStage stg;
   stg.init(bp, it, wave, lane, dv);
-  QCursor cur;
-  cur.first(qp);
+  KvbCursor cur;
+  cur.first(p, qp, it.g, stg.row_bytes, kwg);
 
   if (!dv) {
     RA_LDS char* const qbuf[3] = {(RA_LDS char*)q0_raw, (RA_LDS char*)q1_raw, (RA_LDS char*)q2_raw};
@@ -1084,29 +1144,28 @@ void attn_bwd_kvb_kernel(BwdParams bp) {
     for (int u = 0; u < kD / 16; ++u) st.k[u] = kok ? *(const bf16x8*)(kr + 16 * u + 8 * (lane >> 5)) : bf16x8{};
 #pragma unroll
     for (int db = 0; db < kD / 32; ++db) st.acc[db] = f32x16{};
-    st.pk = f32x16{};
     st.live_prev = false;
-    stg.template issue<kExt, false>(p, cur, it.g, lane, qbuf[0], lbuf[0]);
+    stg.template issue<kExt, false>(p, cur, lane, qbuf[0], lbuf[0]);
     kvb_begin();
     int t = 0;
     for (; t + 5 <= n; t += 6) {
-      kvb_dk_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
-      kvb_dk_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
-      kvb_dk_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
-      kvb_dk_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
-      kvb_dk_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
-      kvb_dk_iter<5, kExt>(st, bp, qp, it, stg, cur, t + 5, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+      kvb_dk_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+      kvb_dk_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+      kvb_dk_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+      kvb_dk_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+      kvb_dk_iter<5, kExt>(st, bp, qp, it, stg, cur, t + 5, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
     }
     // the rest of t = 0 .. n (at most six iterations, the last one t = n)
-    if (t <= n) kvb_dk_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    if (t <= n) kvb_dk_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
     if (t + 1 <= n)
-      kvb_dk_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
     if (t + 2 <= n)
-      kvb_dk_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
     if (t + 3 <= n)
-      kvb_dk_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
     if (t + 4 <= n)
-      kvb_dk_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
     if (!kok) return;
     float* dst = bp.dk + krow * kD;
 #pragma unroll
@@ -1132,26 +1191,26 @@ void attn_bwd_kvb_kernel(BwdParams bp) {
 #pragma unroll
   for (int db = 0; db < kD / 32; ++db) st.acc[db] = f32x16{};
   st.live_prev = false;
-  stg.template issue<kExt, true>(p, cur, it.g, lane, dbuf[0], lbuf[0]);
+  stg.template issue<kExt, true>(p, cur, lane, dbuf[0], lbuf[0]);
   kvb_begin();
   int t = 0;
   for (; t + 5 <= n; t += 6) {
-    kvb_dv_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
-    kvb_dv_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
-    kvb_dv_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
-    kvb_dv_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
-    kvb_dv_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
-    kvb_dv_iter<5, kExt>(st, bp, qp, it, stg, cur, t + 5, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+    kvb_dv_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+    kvb_dv_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+    kvb_dv_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+    kvb_dv_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+    kvb_dv_iter<5, kExt>(st, bp, qp, it, stg, cur, t + 5, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
   }
-  if (t <= n) kvb_dv_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+  if (t <= n) kvb_dv_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
   if (t + 1 <= n)
-    kvb_dv_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
   if (t + 2 <= n)
-    kvb_dv_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
   if (t + 3 <= n)
-    kvb_dv_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
   if (t + 4 <= n)
-    kvb_dv_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
   if (!kok) return;
   float* dst = bp.dv + krow * kD;
 #pragma unroll
