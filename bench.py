@@ -684,7 +684,8 @@ def trace_summary(d, warmup, steps, kernel=KERNEL_NAME):
     out = ["| kernel | calls | avg us | median us | min us | max us | share |", "|---|---|---|---|---|---|---|"]
     for k, v in sorted(per.items(), key=lambda kv: -sum(u for _, u in kv[1])):
         us = [u for _, u in v]
-        out.append(f"| `{k}` | {len(us)} | {np.mean(us):.1f} | {np.median(us):.1f} | {min(us):.1f} | "
+        name = k if len(k) <= 100 else k[:97] + "..."   # library template names run to kilobytes
+        out.append(f"| `{name}` | {len(us)} | {np.mean(us):.1f} | {np.median(us):.1f} | {min(us):.1f} | "
                    f"{max(us):.1f} | {100 * sum(us) / total:.2f}% |")
     step = [u for _, u in sorted(per.get(kernel, []))]
     reps = warmup + 2 * steps + 1

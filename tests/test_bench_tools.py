@@ -45,10 +45,13 @@ def test_trace_summary_takes_only_timed_dispatches(tmp_path):
         t += 100000
     rows.append({"Dispatch_Id": 99, "Kernel_Name": "__amd_rocclr_copyBuffer", "Start_Timestamp": 0,
                  "End_Timestamp": 500})
+    rows.append({"Dispatch_Id": 100, "Kernel_Name": "void lib::k<" + "x" * 300 + ">", "Start_Timestamp": 0,
+                 "End_Timestamp": 400})
     _write(str(tmp_path / "kt" / "kt_kernel_trace.csv"), rows,
            ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
     out = bench.trace_summary(str(tmp_path / "kt"), warmup, steps)
     assert "| `attn_step_bf16_kernel<128, false>` | 12 |" in out
+    assert "| `lib::k<" + "x" * 90 + "...` | 1 |" in out   # long names cut to 100 characters
     assert "timed ring steps: 4 dispatches, mean 2.0 us" in out
     assert "timed per-launch repetitions: 4 dispatches, mean 3.0 us" in out
     assert "2 launches per ring step" in out

@@ -87,6 +87,9 @@ CASES = [
     ("fused_window600_packed_b3", 3, 16, 16, 2048, 2, "zigzag", True, 600, [0, 700, 701, 1500, 2048]),
     # GQA 32/8 through the fused masked kernel (step 0 of each rank)
     ("fused_gqa32x8_window300_b8", 8, 32, 8, 2048, 2, "zigzag", True, 300, None),
+    # non-causal packed sequences through the fused masked kernel: rows see
+    # keys after them, so query tiles sit before the wave's keys
+    ("fused_gqa32x8_packed_noncausal_b8", 8, 32, 8, 2048, 2, "contiguous", False, 0, [0, 700, 701, 1500, 2048]),
 ]
 
 
