@@ -799,43 +799,39 @@ __device__ inline void kvb_copy(const void* base, int nrec, unsigned voff, RA_LD
 struct KvbCursor {
   int hh, span, tile;
   int left;          // rows of the span from the tile's first row on
-  int qrel;          // qglob - kwg (the wave's first key), held in [-2^30, 2^30]
-  long long xoff;    // bytes from (b, row 0, head 0) to the tile's first row, head h, in Q or dO
-  long long soff;    // floats from (b, row 0, head 0) to the same row in L or -delta
-  long long qglob;   // global position of the tile's first row
-  long long kwg;
+  int qrel;          // (tile's first position) - kwg (the wave's first key), held in [-2^30, 2^30]
+  long long xoff;    // bytes from (b, row 0, head 0) to the tile's first row, head h, in Q or dO;
+                     // xoff / kRowB is the same row's offset in L or -delta
 
   __device__ int count() const { return min(32, left); }
-  __device__ void place(const StepParams& p, int g, unsigned row_bytes) {
+  __device__ long long qglob(const StepParams& p) const {
+    return (span ? p.qs_start[1] : p.qs_start[0]) + (long long)tile * 32;
+  }
+  __device__ void place(const StepParams& p, int g, unsigned row_bytes, long long kwg) {
     const long long qin = (long long)tile * 32;
     const long long local0 = (span ? p.qs_off[1] : p.qs_off[0]) + qin;
     const int h = g * p.G + hh;
     left = (int)((span ? p.qs_len[1] : p.qs_len[0]) - qin);
     xoff = local0 * row_bytes + (long long)h * kRowB;
-    soff = local0 * p.Hq + h;
-    qglob = (span ? p.qs_start[1] : p.qs_start[0]) + qin;
-    qrel = (int)max(-(1LL << 30), min(1LL << 30, qglob - kwg));
+    qrel = (int)max(-(1LL << 30), min(1LL << 30, qglob(p) - kwg));
   }
-  __device__ void first(const StepParams& p, const QPlan& qp, int g, unsigned row_bytes, long long kwg_) {
-    kwg = kwg_;
+  __device__ void first(const StepParams& p, const QPlan& qp, int g, unsigned row_bytes, long long kwg) {
     hh = 0;
     span = qp.tend[0] > qp.tbeg[0] ? 0 : 1;
     tile = span ? qp.tbeg[1] : qp.tbeg[0];
-    place(p, g, row_bytes);
+    place(p, g, row_bytes, kwg);
   }
-  __device__ void advance(const StepParams& p, const QPlan& qp, int g, unsigned row_bytes) {
+  __device__ void advance(const StepParams& p, const QPlan& qp, int g, unsigned row_bytes, long long kwg) {
     ++tile;
     if (tile < (span ? qp.tend[1] : qp.tend[0])) {
       left -= 32;
       xoff += 32LL * row_bytes;
-      soff += 32LL * p.Hq;
-      qglob += 32;
       // exact while above -2^29 (a value held at 2^30 stays there: the rows
       // only move on); below, from the positions again
       if (qrel > -(1 << 29))
         qrel = min(qrel + 32, 1 << 30);
       else
-        qrel = (int)max(-(1LL << 30), min(1LL << 30, qglob - kwg));
+        qrel = (int)max(-(1LL << 30), min(1LL << 30, qglob(p) - kwg));
       return;
     }
     if (span == 0 && qp.tend[1] > qp.tbeg[1]) {
@@ -846,7 +842,7 @@ struct KvbCursor {
       span = qp.tend[0] > qp.tbeg[0] ? 0 : 1;
       tile = span ? qp.tbeg[1] : qp.tbeg[0];
     }
-    place(p, g, row_bytes);
+    place(p, g, row_bytes, kwg);
   }
 };
 
@@ -868,29 +864,37 @@ struct KvbStage {
     off[0] = dma_off(w, 0, lane, row_bytes);
     off[1] = dma_off(w, 1, lane, row_bytes);
   }
-  // Query tile c: 32 rows of the group's tensor, and (wave 0) the rows' L at
-  // ldst[0, 256) or -delta at ldst[256, 512); with masks the dK group's waves
-  // 2 and 3 also write the rows' key ranges at ldst[512, 768).  Rows past the
-  // tile's end read 0.
+  // Staging of query tile c in pieces, so that a wave can place them between
+  // the products of a chain: 1, with masks (dK group, waves 2 and 3) the
+  // rows' key ranges to ldst[512, 768), first: with packed sequences they are
+  // looked up in global memory, and the wait for that lookup then covers no
+  // copy of this tile; 2 and 3, the wave's two 1 KB parts of the tile's 32
+  // rows of the group's tensor; 4, (wave 0) the rows' L to ldst[0, 256) or
+  // -delta to ldst[256, 512).  Rows past the tile's end read 0.
   template <bool kExt, bool kDV>
-  __device__ void issue(const StepParams& p, const KvbCursor& c, unsigned lane, RA_LDS char* xdst,
+  __device__ void piece(int k, const StepParams& p, const KvbCursor& c, unsigned lane, RA_LDS char* xdst,
                         RA_LDS char* ldst) const {
     const int count = c.count();
-    const int nrec = (count - 1) * (int)row_bytes + kRowB;
-    // the key ranges first: with packed sequences they are looked up in
-    // global memory, and the wait for that lookup then covers no copy of
-    // this tile
-    if (kExt && !kDV && wave >= 2 && lane < 32) {
-      const long long v = wave == 2 ? key_lo(p, c.qglob + lane) : key_hi(p, c.qglob + lane);
-      ((RA_LDS int*)(ldst + 512))[(wave - 2) * 32 + lane] = (int)max(-(1LL << 30), min(1LL << 30, v - c.qglob));
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) kvb_copy<16>(xbase + c.xoff, nrec, off[i], xdst + (wave * 2 + i) * 1024);
-    if (wave == 0) {
-      const float* src = sbase + c.soff;
+    if (k == 1) {
+      if (kExt && !kDV && wave >= 2 && lane < 32) {
+        const long long qg = c.qglob(p);
+        const long long v = wave == 2 ? key_lo(p, qg + lane) : key_hi(p, qg + lane);
+        ((RA_LDS int*)(ldst + 512))[(wave - 2) * 32 + lane] = (int)max(-(1LL << 30), min(1LL << 30, v - qg));
+      }
+    } else if (k == 2 || k == 3) {
+      const int nrec = (count - 1) * (int)row_bytes + kRowB;
+      kvb_copy<16>(xbase + c.xoff, nrec, off[k - 2], xdst + (wave * 2 + k - 2) * 1024);
+    } else if (k == 4 && wave == 0) {
+      const float* src = sbase + (c.xoff >> 8);  // row offset: xoff / kRowB
       const int nr = ((count - 1) * Hq + 1) * 4;
       kvb_copy<4>(src, nr, lane * (unsigned)Hq * 4u, ldst + (kDV ? 256 : 0));
     }
+  }
+  template <bool kExt, bool kDV>
+  __device__ void issue(const StepParams& p, const KvbCursor& c, unsigned lane, RA_LDS char* xdst,
+                        RA_LDS char* ldst) const {
+#pragma unroll
+    for (int k = 1; k <= 4; ++k) piece<kExt, kDV>(k, p, c, lane, xdst, ldst);
   }
 };
 
@@ -922,20 +926,31 @@ template <int T6, bool kExt>
 __device__ inline void kvb_dk_iter(KvbDk& st, const BwdParams& bp, const QPlan& qp, const KvItem& it,
                                    const KvbStage& stg, KvbCursor& cur, int t, int n, RA_LDS char* const* qbuf,
                                    RA_LDS char* const* lbuf, RA_LDS char* const* pbuf, RA_LDS char* const* gbuf,
-                                   unsigned lane, int wave, bool has_keys) {
+                                   unsigned lane, int wave, long long kwg, bool has_keys) {
   constexpr int CUR = T6 % 3, PRV = (T6 + 2) % 3, NXT = (T6 + 1) % 3, PC = T6 % 2, PP = (T6 + 1) % 2;
   const StepParams& p = bp.s;
   const KvbCursor ci = cur;
-  if (t + 1 < n) {
-    cur.advance(p, qp, it.g, stg.row_bytes);
-    stg.template issue<kExt, false>(p, cur, lane, qbuf[NXT], lbuf[NXT]);
-  }
+  const bool stage = t + 1 < n;
+  // staging of tile t + 1 (piece 0: the cursor's advance), placed between
+  // the dependent products of the score chain when the tile is live (with
+  // masks, whose tiles carry more scalar work, all before it: between the
+  // products it would not fit the scalar registers)
+  auto piece = [&](int k) {
+    if (!stage) return;
+    if (k == 0)
+      cur.advance(p, qp, it.g, stg.row_bytes, kwg);
+    else
+      stg.template piece<kExt, false>(k, p, cur, lane, qbuf[NXT], lbuf[NXT]);
+  };
   const int L = (int)(lane >> 5);
-  bool live = false;
+  const bool live = t < n && kvb_live(p, ci, has_keys);
   f32x16& pk = st.pk[PC];  // tile t's P, read next iteration only if live
-  if (t < n) {
-    live = kvb_live(p, ci, has_keys);
-    if (live) {
+  if (kExt || !live) {
+#pragma unroll
+    for (int k = 0; k <= 4; ++k) piece(k);
+  }
+  if (live) {
+    {
       // every operand read issued before the product chain (the chain then
       // waits only for the read it needs next)
       const unsigned rb = row_base_sigma(lane);
@@ -945,8 +960,12 @@ __device__ inline void kvb_dk_iter(KvbDk& st, const BwdParams& bp, const QPlan& 
       __builtin_amdgcn_sched_barrier(0);
       f32x16 s = f32x16{};
 #pragma unroll
-      for (int u = 0; u < kD / 16; ++u) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], st.k[u], s, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int u = 0; u < kD / 16; ++u) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], st.k[u], s, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!kExt && u <= 4) piece(u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // rows of register r: 16(r/8) + 8L + r%8 of the tile; the lane's key
       const int key = (int)(lane & 31u);
       const RA_LDS int* rt = (const RA_LDS int*)(lbuf[CUR] + 512);
@@ -1031,17 +1050,26 @@ template <int T6, bool kExt>
 __device__ inline void kvb_dv_iter(KvbDv& st, const BwdParams& bp, const QPlan& qp, const KvItem& it,
                                    const KvbStage& stg, KvbCursor& cur, int t, int n, RA_LDS char* const* dbuf,
                                    RA_LDS char* const* lbuf, RA_LDS char* const* pbuf, RA_LDS char* const* gbuf,
-                                   unsigned lane, int wave, bool has_keys) {
+                                   unsigned lane, int wave, long long kwg, bool has_keys) {
   constexpr int CUR = T6 % 3, PRV = (T6 + 2) % 3, NXT = (T6 + 1) % 3, PC = T6 % 2, PP = (T6 + 1) % 2;
   const StepParams& p = bp.s;
   const KvbCursor ci = cur;
-  if (t + 1 < n) {
-    cur.advance(p, qp, it.g, stg.row_bytes);
-    stg.template issue<kExt, true>(p, cur, lane, dbuf[NXT], lbuf[NXT]);
+  const bool stage = t + 1 < n;
+  // staging of tile t + 1, placed between the dependent products of the dP
+  // chain when the tile is live (with masks, all before it)
+  auto piece = [&](int k) {
+    if (!stage) return;
+    if (k == 0)
+      cur.advance(p, qp, it.g, stg.row_bytes, kwg);
+    else
+      stg.template piece<kExt, true>(k, p, cur, lane, dbuf[NXT], lbuf[NXT]);
+  };
+  const bool live = t < n && kvb_live(p, ci, has_keys);
+  if (kExt || !live) {
+#pragma unroll
+    for (int k = 0; k <= 4; ++k) piece(k);
   }
-  bool live = false;
-  if (t < n) {
-    live = kvb_live(p, ci, has_keys);
+  {
     if (live) {
       // dP - delta: the chain starts from the rows' -delta (register r of the
       // lane is row 16(r/8) + 8L + r%8)
@@ -1061,8 +1089,12 @@ __device__ inline void kvb_dv_iter(KvbDv& st, const BwdParams& bp, const QPlan& 
       for (int u = 0; u < kD / 16; ++u) b[u] = __builtin_bit_cast(bf16x8, lds_load16(dbuf[CUR], rb ^ (32u * u)));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < kD / 16; ++u) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[u], st.v[u], dp, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int u = 0; u < kD / 16; ++u) {
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[u], st.v[u], dp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!kExt && u <= 4) piece(u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       RA_LDS f32x4* g = (RA_LDS f32x4*)(gbuf[PC] + wave * 4096) + lane;
 #pragma unroll
       for (int k = 0; k < 4; ++k) g[k * 64] = f32x4{dp[4 * k], dp[4 * k + 1], dp[4 * k + 2], dp[4 * k + 3]};
@@ -1149,23 +1181,23 @@ void attn_bwd_kvb_kernel(BwdParams bp) {
     kvb_begin();
     int t = 0;
     for (; t + 5 <= n; t += 6) {
-      kvb_dk_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
-      kvb_dk_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
-      kvb_dk_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
-      kvb_dk_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
-      kvb_dk_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
-      kvb_dk_iter<5, kExt>(st, bp, qp, it, stg, cur, t + 5, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+      kvb_dk_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+      kvb_dk_iter<5, kExt>(st, bp, qp, it, stg, cur, t + 5, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
     }
     // the rest of t = 0 .. n (at most six iterations, the last one t = n)
-    if (t <= n) kvb_dk_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+    if (t <= n) kvb_dk_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
     if (t + 1 <= n)
-      kvb_dk_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+      kvb_dk_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
     if (t + 2 <= n)
-      kvb_dk_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+      kvb_dk_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
     if (t + 3 <= n)
-      kvb_dk_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+      kvb_dk_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
     if (t + 4 <= n)
-      kvb_dk_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, qbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+      kvb_dk_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, qbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
     if (!kok) return;
     float* dst = bp.dk + krow * kD;
 #pragma unroll
@@ -1195,22 +1227,22 @@ void attn_bwd_kvb_kernel(BwdParams bp) {
   kvb_begin();
   int t = 0;
   for (; t + 5 <= n; t += 6) {
-    kvb_dv_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
-    kvb_dv_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
-    kvb_dv_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
-    kvb_dv_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
-    kvb_dv_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
-    kvb_dv_iter<5, kExt>(st, bp, qp, it, stg, cur, t + 5, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+    kvb_dv_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
+    kvb_dv_iter<5, kExt>(st, bp, qp, it, stg, cur, t + 5, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
   }
-  if (t <= n) kvb_dv_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+  if (t <= n) kvb_dv_iter<0, kExt>(st, bp, qp, it, stg, cur, t, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
   if (t + 1 <= n)
-    kvb_dv_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+    kvb_dv_iter<1, kExt>(st, bp, qp, it, stg, cur, t + 1, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
   if (t + 2 <= n)
-    kvb_dv_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+    kvb_dv_iter<2, kExt>(st, bp, qp, it, stg, cur, t + 2, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
   if (t + 3 <= n)
-    kvb_dv_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+    kvb_dv_iter<3, kExt>(st, bp, qp, it, stg, cur, t + 3, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
   if (t + 4 <= n)
-    kvb_dv_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, dbuf, lbuf, pbuf, gbuf, lane, wave, has_keys);
+    kvb_dv_iter<4, kExt>(st, bp, qp, it, stg, cur, t + 4, n, dbuf, lbuf, pbuf, gbuf, lane, wave, kwg, has_keys);
   if (!kok) return;
   float* dst = bp.dv + krow * kD;
 #pragma unroll
