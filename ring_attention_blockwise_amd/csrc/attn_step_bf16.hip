@@ -94,7 +94,10 @@ struct WaveState {
 
 // Per-thread addresses.  They are cheap to derive from the thread id, so each
 // tile derives them again from a laundered copy of it instead of keeping them
-// in registers across the loop.
+// in registers across the loop; the four-wave kernel keeps one, the V read
+// base, for the whole item (derived per tile it cost about 15 vector
+// instructions of a tile's ~140; the key-split kernels, short of registers,
+// still derive it per tile).
 template <int D>
 struct Lane {
   typedef Layout<D> Ly;
@@ -201,7 +204,7 @@ template <int D, int PAR, bool kExt, bool kKS>
 __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const TilePlan& tp, const WorkItem& wi,
                                  const Stager<D, kKS || kExt>& st, TileCursor& cur, int t, int te, unsigned phase,
                                  RA_LDS char* const* kbuf, RA_LDS char* const* vbuf, const RA_LDS int* row_lo,
-                                 const RA_LDS int* row_hi, int lane, int wave) {
+                                 const RA_LDS int* row_hi, int lane, int wave, unsigned vb0) {
   if (kKS && t >= te) {
     __syncthreads();
     return;
@@ -353,7 +356,6 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
   }
 
   __builtin_amdgcn_sched_barrier(0);
-  const unsigned vb0 = ln.vb0();
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -414,11 +416,11 @@ __device__ __attribute__((always_inline)) inline void fwd_pass(WaveState<D>& ws,
   const int tend = kKS ? tb + iters : tp.n;
   int t = kKS ? tb : 0;
   for (; t + 1 < tend; t += 2) {
-    step_tile<D, 0, kExt, kKS>(ws, p, tp, wi, st, cur, t, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave);
-    step_tile<D, 1, kExt, kKS>(ws, p, tp, wi, st, cur, t + 1, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave);
+    step_tile<D, 0, kExt, kKS>(ws, p, tp, wi, st, cur, t, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave, Lane<D>((unsigned)(p.Hkv * D * 2), wave).vb0());
+    step_tile<D, 1, kExt, kKS>(ws, p, tp, wi, st, cur, t + 1, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave, Lane<D>((unsigned)(p.Hkv * D * 2), wave).vb0());
   }
   if (t < tend)
-    step_tile<D, 0, kExt, kKS>(ws, p, tp, wi, st, cur, t, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave);
+    step_tile<D, 0, kExt, kKS>(ws, p, tp, wi, st, cur, t, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave, Lane<D>((unsigned)(p.Hkv * D * 2), wave).vb0());
 }
 
 // The kernel above: four waves (256 query rows, 64 per wave) walk every key
@@ -488,14 +490,16 @@ void attn_step_bf16_kernel(StepParams p) {
   __syncthreads();
 
   // main loop, unrolled by two so that buffers are named statically:
-  // iteration t uses parity t mod 2.
+  // iteration t uses parity t mod 2.  The V read base stays in a register for
+  // the whole item.
+  const unsigned vb0 = Lane<D>((unsigned)(p.Hkv * D * 2), wave).vb0();
   int t = 0;
   for (; t + 1 < tp.n; t += 2) {
-    step_tile<D, 0, kExt, false>(ws, p, tp, wi, st, cur, t, tp.n, 0u, kbuf, vbuf, row_lo, row_hi, lane, wave);
+    step_tile<D, 0, kExt, false>(ws, p, tp, wi, st, cur, t, tp.n, 0u, kbuf, vbuf, row_lo, row_hi, lane, wave, vb0);
     step_tile<D, 1, kExt, false>(ws, p, tp, wi, st, cur, t + 1, tp.n, 0u, kbuf, vbuf, row_lo, row_hi, lane,
-                                  wave);
+                                  wave, vb0);
   }
-  if (t < tp.n) step_tile<D, 0, kExt, false>(ws, p, tp, wi, st, cur, t, tp.n, 0u, kbuf, vbuf, row_lo, row_hi, lane, wave);
+  if (t < tp.n) step_tile<D, 0, kExt, false>(ws, p, tp, wi, st, cur, t, tp.n, 0u, kbuf, vbuf, row_lo, row_hi, lane, wave, vb0);
 
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
