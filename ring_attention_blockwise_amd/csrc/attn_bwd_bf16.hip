@@ -55,6 +55,13 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 constexpr int kD = 128;
+
+// Tag for the two instantiations of a tile body, with and without the
+// per-row key-range select.
+template <bool B>
+struct KvbSel {
+  static constexpr bool value = B;
+};
 constexpr int kThreads = 256;
 constexpr int kRowB = 2 * kD;               // bytes of one bf16 row
 constexpr int kTileB = 32 * kRowB;          // a 32-row tile
@@ -546,43 +553,63 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
     unsigned b0, b1;
     tr_bases(lane, b0, b1);
     // one 16-row half at a time: P (and dS) of rows 16hf .. 16hf+15, then the
-    // product over those rows
+    // product over those rows; kSel: with the per-row key-range select
+    // (masks; not on tiles whose every row sees all the wave's keys)
+    auto halves = [&](auto sel) {
+      constexpr bool kSel = decltype(sel)::value;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const f32x4 l0 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L);
-      const f32x4 l1 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L + 4);
-      const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-      int lo[8], hi[8];
-      if (kExt) {
-        const i32x4 a0 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L);
-        const i32x4 a1 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L + 4);
-        const i32x4 c0 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L);
-        const i32x4 c1 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L + 4);
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 l0 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L);
+        const f32x4 l1 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L + 4);
+        const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+        int lo[8], hi[8];
+        if (kSel) {
+          const i32x4 a0 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L);
+          const i32x4 a1 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L + 4);
+          const i32x4 c0 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L);
+          const i32x4 c1 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lo[e] = a0[e], lo[e + 4] = a1[e], hi[e] = c0[e], hi[e + 4] = c1[e];
+          for (int e = 0; e < 4; ++e) lo[e] = a0[e], lo[e + 4] = a1[e], hi[e] = c0[e], hi[e + 4] = c1[e];
+        }
+        f32x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // No guard for rows past the tile's end: their Q, dO, L and delta
+          // were staged as zeros, so P = 1 there multiplies zero rows (and dS
+          // = 0).  L is finite on every real row (each row sees at least its
+          // own key), so P needs no -inf case; under masks a key outside the
+          // row's range gets exponent -inf.  A select, not a branch, before
+          // exp2.
+          float a = __builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e);
+          if (kSel) a = (lo[e] <= dk && dk <= hi[e]) ? a : kNegInf;
+          const float pr = __builtin_amdgcn_exp2f(a);
+          x[e] = kDK ? pr * dp[8 * hf + e] : pr;
+        }
+        const bf16x8 xb = __builtin_convertvector(x, bf16x8);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db) {
+          const unsigned o0 = (b0 ^ (64u * db)) + 16u * kRowB * hf, o1 = (b1 ^ (64u * db)) + 16u * kRowB * hf;
+          const bf16x8 a = tr_read(kDK ? qbuf[CUR] : dbuf[CUR], o0, o1);
+          st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb, st.acc[db], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      f32x8 x;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // No guard for rows past the tile's end: their Q, dO, L and delta
-        // were staged as zeros, so P = 1 there multiplies zero rows (and dS =
-        // 0).  L is finite on every real row (each row sees at least its own
-        // key), so P needs no -inf case; under masks a key outside the row's
-        // range gets exponent -inf.  A select, not a branch, before exp2.
-        float a = __builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e);
-        if (kExt) a = (lo[e] <= dk && dk <= hi[e]) ? a : kNegInf;
-        const float pr = __builtin_amdgcn_exp2f(a);
-        x[e] = kDK ? pr * dp[8 * hf + e] : pr;
-      }
-      const bf16x8 xb = __builtin_convertvector(x, bf16x8);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int db = 0; db < kD / 32; ++db) {
-        const unsigned o0 = (b0 ^ (64u * db)) + 16u * kRowB * hf, o1 = (b1 ^ (64u * db)) + 16u * kRowB * hf;
-        const bf16x8 a = tr_read(kDK ? qbuf[CUR] : dbuf[CUR], o0, o1);
-        st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb, st.acc[db], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (kExt && !kDK) {
+      // the ranges never move left along the rows: every row sees the wave's
+      // keys (relative positions dk - key .. dk - key + 31) iff the last
+      // row's lower end and the first row's upper end do.  (The dK kernel,
+      // with dP's registers live as well, would spill with both bodies.)
+      const int lo_last = __builtin_amdgcn_readfirstlane(rt[31]);
+      const int hi_first = __builtin_amdgcn_readfirstlane(rt[32]);
+      const int k0 = __builtin_amdgcn_readfirstlane(dk - key);
+      if (lo_last <= k0 && k0 + 31 <= hi_first)
+        halves(KvbSel<false>{});
+      else
+        halves(KvbSel<true>{});
+    } else {
+      halves(KvbSel<kExt>{});
     }
   }
   wait_loads();
@@ -977,32 +1004,50 @@ __device__ inline void kvb_dk_iter(KvbDk& st, const BwdParams& bp, const QPlan& 
         for (int r = 0; r < 16; ++r) s[r] = neg_inf_select(dd + 16 * (r >> 3) + (r & 7), s[r]);
       }
       const RA_LDS float* lt = (const RA_LDS float*)lbuf[CUR];
+      // P of the tile; kSel: with the per-row key-range select (masks; not
+      // on tiles whose every row sees all the wave's keys)
+      auto probabilities = [&](auto sel) {
+        constexpr bool kSel = decltype(sel)::value;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const f32x4 l0 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L);
-        const f32x4 l1 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L + 4);
-        const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-        int lo[8], hi[8];
-        if (kExt) {
-          const i32x4 a0 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L);
-          const i32x4 a1 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L + 4);
-          const i32x4 c0 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L);
-          const i32x4 c1 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L + 4);
+        for (int hf = 0; hf < 2; ++hf) {
+          const f32x4 l0 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L);
+          const f32x4 l1 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L + 4);
+          const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+          int lo[8], hi[8];
+          if (kSel) {
+            const i32x4 a0 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L);
+            const i32x4 a1 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L + 4);
+            const i32x4 c0 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L);
+            const i32x4 c1 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L + 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) lo[e] = a0[e], lo[e + 4] = a1[e], hi[e] = c0[e], hi[e + 4] = c1[e];
+            for (int e = 0; e < 4; ++e) lo[e] = a0[e], lo[e + 4] = a1[e], hi[e] = c0[e], hi[e + 4] = c1[e];
+          }
+          f32x8 xp;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            // rows past the tile's end were staged as zeros (P = 1 times zero
+            // rows); L is finite on every real row; a key outside the row's
+            // range gets exponent -inf (a select before exp2)
+            float a = __builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e);
+            if (kSel) a = (lo[e] <= dk && dk <= hi[e]) ? a : kNegInf;
+            xp[e] = __builtin_amdgcn_exp2f(a);
+            pk[8 * hf + e] = xp[e];
+          }
+          *(RA_LDS bf16x8*)(pbuf[PC] + (wave * 2 + hf) * 1024 + lane * 16) = __builtin_convertvector(xp, bf16x8);
         }
-        f32x8 xp;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // rows past the tile's end were staged as zeros (P = 1 times zero
-          // rows); L is finite on every real row; a key outside the row's
-          // range gets exponent -inf (a select before exp2)
-          float a = __builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e);
-          if (kExt) a = (lo[e] <= dk && dk <= hi[e]) ? a : kNegInf;
-          xp[e] = __builtin_amdgcn_exp2f(a);
-          pk[8 * hf + e] = xp[e];
-        }
-        *(RA_LDS bf16x8*)(pbuf[PC] + (wave * 2 + hf) * 1024 + lane * 16) = __builtin_convertvector(xp, bf16x8);
+      };
+      if constexpr (kExt) {
+        // the ranges never move left along the rows, so every row sees the
+        // wave's keys (relative positions -qrel .. 31 - qrel) iff the last
+        // row's lower end and the first row's upper end do
+        const int lo_last = __builtin_amdgcn_readfirstlane(rt[31]);
+        const int hi_first = __builtin_amdgcn_readfirstlane(rt[32]);
+        if (lo_last <= -ci.qrel && 31 - ci.qrel <= hi_first)
+          probabilities(KvbSel<false>{});
+        else
+          probabilities(KvbSel<true>{});
+      } else {
+        probabilities(KvbSel<false>{});
       }
     }
   }
