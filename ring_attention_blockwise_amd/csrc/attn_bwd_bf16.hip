@@ -781,8 +781,8 @@ void attn_bwd_kv_kernel(BwdParams bp) {
 // products apiece.  Q, dO, L and -delta are staged in three stages (tile t
 // is read in iterations t and t + 1), P and dP - delta in two.
 
-// Copy through the buffer unit into LDS at dst + 4 kBytes * lane (kBytes 16
-// or 4 per lane, lane offset voff into a record of nrec bytes at base), issued
+// Copy through the buffer unit into LDS, lane i's kBytes (16 or 4) from byte
+// voff of a record of nrec bytes at base to dst + kBytes * i, issued
 // from inline assembly so that the compiler does not see an LDS write in
 // flight: it cannot tell this kernel's staged buffers apart from the ones its
 // waves are reading and would otherwise wait for every copy before those
