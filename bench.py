@@ -357,13 +357,14 @@ def masked_pairs(w, rank, window):
     return int(np.minimum(t + 1, window).sum())
 
 
-def time_window(ra, w, rank, window, reps=5):
+def time_window(ra, w, rank, window, reps=10, warmup=3):
     """The same rank's ring with a causal sliding window: masked tiles at both
     ends of each row's key range, hidden tiles and steps skipped."""
     import torch
     q, ks, vs, o, lse = build_inputs(ra, w, rank)
     kw = dict(S=w.S, P=w.P, rank=rank, order=w.order, causal=True, scale=w.scale, window=window)
-    ra.ra_rank_forward_masked(q, ks, vs, o, lse, **kw)
+    for _ in range(warmup):
+        ra.ra_rank_forward_masked(q, ks, vs, o, lse, **kw)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
@@ -420,15 +421,17 @@ def time_graph(ra, name, rank, reps=20):
             "frac_peak": flops / (res["graph"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def time_config(ra, name, rank, reps=5):
+def time_config(ra, name, rank, reps=10, warmup=3):
     """Another workload's ring: rank ``rank``'s forward (all steps, fused
-    merges), eager, HIP events around each call; mean, median and min."""
+    merges), eager, HIP events around each call after ``warmup`` untimed
+    calls on the freshly allocated inputs; mean, median and min."""
     import torch
     from seeded_inputs import workload
     w = workload(name)
     q, ks, vs, o, lse = build_inputs(ra, w, rank)
     kw = dict(S=w.S, P=w.P, rank=rank, order=w.order, causal=w.causal, scale=w.scale)
-    ra.ra_rank_forward(q, ks, vs, o, lse, **kw)
+    for _ in range(warmup):
+        ra.ra_rank_forward(q, ks, vs, o, lse, **kw)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
