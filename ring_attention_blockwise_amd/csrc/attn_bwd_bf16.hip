@@ -977,78 +977,76 @@ __device__ inline void kvb_dk_iter(KvbDk& st, const BwdParams& bp, const QPlan& 
     for (int k = 0; k <= 4; ++k) piece(k);
   }
   if (live) {
-    {
-      // every operand read issued before the product chain (the chain then
-      // waits only for the read it needs next)
-      const unsigned rb = row_base_sigma(lane);
-      bf16x8 a[kD / 16];
+    // every operand read issued before the product chain (the chain then
+    // waits only for the read it needs next)
+    const unsigned rb = row_base_sigma(lane);
+    bf16x8 a[kD / 16];
 #pragma unroll
-      for (int u = 0; u < kD / 16; ++u) a[u] = __builtin_bit_cast(bf16x8, lds_load16(qbuf[CUR], rb ^ (32u * u)));
+    for (int u = 0; u < kD / 16; ++u) a[u] = __builtin_bit_cast(bf16x8, lds_load16(qbuf[CUR], rb ^ (32u * u)));
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int u = 0; u < kD / 16; ++u) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], st.k[u], s, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      f32x16 s = f32x16{};
+      if (!kExt && u <= 4) piece(u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // rows of register r: 16(r/8) + 8L + r%8 of the tile; the lane's key
+    const int key = (int)(lane & 31u);
+    const RA_LDS int* rt = (const RA_LDS int*)(lbuf[CUR] + 512);
+    const int dk = kExt ? key - ci.qrel : 0;
+    if (!kExt && p.causal && ci.qrel < 31) {
+      // row i sees key j iff qglob + i >= kwg + j
+      const int dd = max(-1024, min(1024, ci.qrel)) + 8 * L - key;
 #pragma unroll
-      for (int u = 0; u < kD / 16; ++u) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], st.k[u], s, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (!kExt && u <= 4) piece(u);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // rows of register r: 16(r/8) + 8L + r%8 of the tile; the lane's key
-      const int key = (int)(lane & 31u);
-      const RA_LDS int* rt = (const RA_LDS int*)(lbuf[CUR] + 512);
-      const int dk = kExt ? key - ci.qrel : 0;
-      if (!kExt && p.causal && ci.qrel < 31) {
-        // row i sees key j iff qglob + i >= kwg + j
-        const int dd = max(-1024, min(1024, ci.qrel)) + 8 * L - key;
+      for (int r = 0; r < 16; ++r) s[r] = neg_inf_select(dd + 16 * (r >> 3) + (r & 7), s[r]);
+    }
+    const RA_LDS float* lt = (const RA_LDS float*)lbuf[CUR];
+    // P of the tile; kSel: with the per-row key-range select (masks; not
+    // on tiles whose every row sees all the wave's keys)
+    auto probabilities = [&](auto sel) {
+      constexpr bool kSel = decltype(sel)::value;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = neg_inf_select(dd + 16 * (r >> 3) + (r & 7), s[r]);
-      }
-      const RA_LDS float* lt = (const RA_LDS float*)lbuf[CUR];
-      // P of the tile; kSel: with the per-row key-range select (masks; not
-      // on tiles whose every row sees all the wave's keys)
-      auto probabilities = [&](auto sel) {
-        constexpr bool kSel = decltype(sel)::value;
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 l0 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L);
+        const f32x4 l1 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L + 4);
+        const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+        int lo[8], hi[8];
+        if (kSel) {
+          const i32x4 a0 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L);
+          const i32x4 a1 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L + 4);
+          const i32x4 c0 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L);
+          const i32x4 c1 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L + 4);
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const f32x4 l0 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L);
-          const f32x4 l1 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L + 4);
-          const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-          int lo[8], hi[8];
-          if (kSel) {
-            const i32x4 a0 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L);
-            const i32x4 a1 = *(const RA_LDS i32x4*)(rt + 16 * hf + 8 * L + 4);
-            const i32x4 c0 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L);
-            const i32x4 c1 = *(const RA_LDS i32x4*)(rt + 32 + 16 * hf + 8 * L + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) lo[e] = a0[e], lo[e + 4] = a1[e], hi[e] = c0[e], hi[e + 4] = c1[e];
-          }
-          f32x8 xp;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            // rows past the tile's end were staged as zeros (P = 1 times zero
-            // rows); L is finite on every real row; a key outside the row's
-            // range gets exponent -inf (a select before exp2)
-            float a = __builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e);
-            if (kSel) a = (lo[e] <= dk && dk <= hi[e]) ? a : kNegInf;
-            xp[e] = __builtin_amdgcn_exp2f(a);
-            pk[8 * hf + e] = xp[e];
-          }
-          *(RA_LDS bf16x8*)(pbuf[PC] + (wave * 2 + hf) * 1024 + lane * 16) = __builtin_convertvector(xp, bf16x8);
+          for (int e = 0; e < 4; ++e) lo[e] = a0[e], lo[e + 4] = a1[e], hi[e] = c0[e], hi[e + 4] = c1[e];
         }
-      };
-      if constexpr (kExt) {
-        // the ranges never move left along the rows, so every row sees the
-        // wave's keys (relative positions -qrel .. 31 - qrel) iff the last
-        // row's lower end and the first row's upper end do
-        const int lo_last = __builtin_amdgcn_readfirstlane(rt[31]);
-        const int hi_first = __builtin_amdgcn_readfirstlane(rt[32]);
-        if (lo_last <= -ci.qrel && 31 - ci.qrel <= hi_first)
-          probabilities(KvbSel<false>{});
-        else
-          probabilities(KvbSel<true>{});
-      } else {
-        probabilities(KvbSel<false>{});
+        f32x8 xp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // rows past the tile's end were staged as zeros (P = 1 times zero
+          // rows); L is finite on every real row; a key outside the row's
+          // range gets exponent -inf (a select before exp2)
+          float a = __builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e);
+          if (kSel) a = (lo[e] <= dk && dk <= hi[e]) ? a : kNegInf;
+          xp[e] = __builtin_amdgcn_exp2f(a);
+          pk[8 * hf + e] = xp[e];
+        }
+        *(RA_LDS bf16x8*)(pbuf[PC] + (wave * 2 + hf) * 1024 + lane * 16) = __builtin_convertvector(xp, bf16x8);
       }
+    };
+    if constexpr (kExt) {
+      // the ranges never move left along the rows, so every row sees the
+      // wave's keys (relative positions -qrel .. 31 - qrel) iff the last
+      // row's lower end and the first row's upper end do
+      const int lo_last = __builtin_amdgcn_readfirstlane(rt[31]);
+      const int hi_first = __builtin_amdgcn_readfirstlane(rt[32]);
+      if (lo_last <= -ci.qrel && 31 - ci.qrel <= hi_first)
+        probabilities(KvbSel<false>{});
+      else
+        probabilities(KvbSel<true>{});
+    } else {
+      probabilities(KvbSel<false>{});
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -1114,36 +1112,34 @@ __device__ inline void kvb_dv_iter(KvbDv& st, const BwdParams& bp, const QPlan& 
 #pragma unroll
     for (int k = 0; k <= 4; ++k) piece(k);
   }
-  {
-    if (live) {
-      // dP - delta: the chain starts from the rows' -delta (register r of the
-      // lane is row 16(r/8) + 8L + r%8)
-      const int L = (int)(lane >> 5);
-      const RA_LDS float* lt = (const RA_LDS float*)lbuf[CUR];
-      f32x16 dp;
+  if (live) {
+    // dP - delta: the chain starts from the rows' -delta (register r of the
+    // lane is row 16(r/8) + 8L + r%8)
+    const int L = (int)(lane >> 5);
+    const RA_LDS float* lt = (const RA_LDS float*)lbuf[CUR];
+    f32x16 dp;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const f32x4 t0 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L);
-        const f32x4 t1 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L + 4);
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 t0 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L);
+      const f32x4 t1 = *(const RA_LDS f32x4*)(lt + 64 + 16 * hf + 8 * L + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dp[8 * hf + e] = t0[e], dp[8 * hf + 4 + e] = t1[e];
-      }
-      const unsigned rb = row_base_sigma(lane);
-      bf16x8 b[kD / 16];
-#pragma unroll
-      for (int u = 0; u < kD / 16; ++u) b[u] = __builtin_bit_cast(bf16x8, lds_load16(dbuf[CUR], rb ^ (32u * u)));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < kD / 16; ++u) {
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[u], st.v[u], dp, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (!kExt && u <= 4) piece(u);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      RA_LDS f32x4* g = (RA_LDS f32x4*)(gbuf[PC] + wave * 4096) + lane;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) g[k * 64] = f32x4{dp[4 * k], dp[4 * k + 1], dp[4 * k + 2], dp[4 * k + 3]};
+      for (int e = 0; e < 4; ++e) dp[8 * hf + e] = t0[e], dp[8 * hf + 4 + e] = t1[e];
     }
+    const unsigned rb = row_base_sigma(lane);
+    bf16x8 b[kD / 16];
+#pragma unroll
+    for (int u = 0; u < kD / 16; ++u) b[u] = __builtin_bit_cast(bf16x8, lds_load16(dbuf[CUR], rb ^ (32u * u)));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kD / 16; ++u) {
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[u], st.v[u], dp, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!kExt && u <= 4) piece(u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    RA_LDS f32x4* g = (RA_LDS f32x4*)(gbuf[PC] + wave * 4096) + lane;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) g[k * 64] = f32x4{dp[4 * k], dp[4 * k + 1], dp[4 * k + 2], dp[4 * k + 3]};
   }
   __builtin_amdgcn_sched_barrier(0);
   if (t > 0 && st.live_prev) {
