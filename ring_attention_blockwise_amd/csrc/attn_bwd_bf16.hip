@@ -469,8 +469,8 @@ struct KvStage {
       const float* src = (wave == 0 ? lbase : tbase) + local0 * Hq + h;
       const int nr = ((count - 1) * Hq + 1) * 4;
       const auto rl = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nr, kRsrcWord3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (RA_LDS void*)(ldst + wave * 256), 4, (int)(lane * (unsigned)Hq * 4u),
-                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (RA_LDS void*)(ldst + wave * 256), 4,
+                                               (int)(lane * (unsigned)Hq * 4u), 0, 0, 0);
     } else if (kExt && lane < 32) {
       // masks: key range [lo, hi] of each row, relative to the tile's first
       // row (wave 2: lo, wave 3: hi), at ldst[512, 768)
@@ -619,9 +619,11 @@ __device__ inline void kv_tile(KvState<kDK>& st, const BwdParams& bp, const QPla
 // One key tile's pass over its query tiles by one group of four waves (GRP),
 // tiles [tb, te) of the list; returns the accumulators in st.
 template <bool kDK, bool kExt>
-__device__ __attribute__((always_inline)) inline void kv_pass(KvState<kDK>& st, const BwdParams& bp, const QPlan& qp, const KvItem& it, int tb,
-                               int te, int iters, RA_LDS char* const* qbuf, RA_LDS char* const* dbuf,
-                               RA_LDS char* const* lbuf, unsigned lane, int wave) {
+__device__ __attribute__((always_inline)) inline void kv_pass(KvState<kDK>& st, const BwdParams& bp,
+                                                               const QPlan& qp, const KvItem& it, int tb, int te,
+                                                               int iters, RA_LDS char* const* qbuf,
+                                                               RA_LDS char* const* dbuf, RA_LDS char* const* lbuf,
+                                                               unsigned lane, int wave) {
   const StepParams& p = bp.s;
   KvStage stg;
   stg.init(bp, it, wave, lane);
@@ -1072,7 +1074,8 @@ __device__ inline void kvb_dk_iter(KvbDk& st, const BwdParams& bp, const QPlan& 
       }
       const bf16x8 xb = __builtin_convertvector(x, bf16x8);
 #pragma unroll
-      for (int db = 0; db < kD / 32; ++db) st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[db], xb, st.acc[db], 0, 0, 0);
+      for (int db = 0; db < kD / 32; ++db)
+        st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[db], xb, st.acc[db], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -1155,7 +1158,8 @@ __device__ inline void kvb_dv_iter(KvbDv& st, const BwdParams& bp, const QPlan& 
         dt[db] = tr_read(dbuf[PRV], (b0 ^ (64u * db)) + 16u * kRowB * hf, (b1 ^ (64u * db)) + 16u * kRowB * hf);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < kD / 32; ++db) st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt[db], xb, st.acc[db], 0, 0, 0);
+      for (int db = 0; db < kD / 32; ++db)
+        st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt[db], xb, st.acc[db], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }

@@ -160,7 +160,8 @@ hipError_t launch_simt_delta(long long rows, int D, int dtype, const void* dout,
   if (rows <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)((rows + 255) / 256);
   if (dtype == 0 && D == 64)
-    hipLaunchKernelGGL((simt_delta_kernel<float, 64>), dim3(blocks), dim3(256), 0, s, rows, (const float*)dout, o, delta);
+    hipLaunchKernelGGL((simt_delta_kernel<float, 64>), dim3(blocks), dim3(256), 0, s, rows, (const float*)dout, o,
+                       delta);
   else if (dtype == 0 && D == 128)
     hipLaunchKernelGGL((simt_delta_kernel<float, 128>), dim3(blocks), dim3(256), 0, s, rows, (const float*)dout, o,
                        delta);

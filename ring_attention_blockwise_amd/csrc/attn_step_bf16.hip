@@ -219,10 +219,12 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
   // Two wave sets share each SIMD (two workgroups of a CU, or the two groups
   // of an eight-wave workgroup); the wave arbiter favours the older, which
   // then finishes its (equal) work long before the younger.  Swapping the
-  // issue priority every 32 tiles, in opposite phase for the two (dispatch
-  // fills one slot on each of the 256 CUs before the second), lets both
-  // progress at about the same rate.
-  if ((((unsigned)t >> 5) ^ (kKS ? phase : (blockIdx.x >> 8))) & 1u)
+  // issue priority every 64 tiles (32 in the key split, whose wave sets walk
+  // fewer tiles), in opposite phase for the two (dispatch fills one slot on
+  // each of the 256 CUs before the second), lets both progress at about the
+  // same rate.  Measured on the 131k and 64k rings: a period of 64 or 128
+  // tiles beats 32 by ~1% and 8 or 16 do not; 256 or no swap lose 3-4%.
+  if ((((unsigned)t >> (kKS ? 5 : 6)) ^ (kKS ? phase : (blockIdx.x >> 8))) & 1u)
     __builtin_amdgcn_s_setprio(1);
   else
     __builtin_amdgcn_s_setprio(0);
@@ -362,7 +364,8 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
     for (int db = 0; db < D / 32; ++db) {
       const unsigned off = (vb0 ^ (64u * db)) + 16 * hf * Layout<D>::kVStride;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vbuf[PAR] + off));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vbuf[PAR] + off + 4 * Layout<D>::kVStride));
+      const i16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS i16x4*)(vbuf[PAR] + off + 4 * Layout<D>::kVStride));
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb)
@@ -416,11 +419,14 @@ __device__ __attribute__((always_inline)) inline void fwd_pass(WaveState<D>& ws,
   const int tend = kKS ? tb + iters : tp.n;
   int t = kKS ? tb : 0;
   for (; t + 1 < tend; t += 2) {
-    step_tile<D, 0, kExt, kKS>(ws, p, tp, wi, st, cur, t, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave, Lane<D>((unsigned)(p.Hkv * D * 2), wave).vb0());
-    step_tile<D, 1, kExt, kKS>(ws, p, tp, wi, st, cur, t + 1, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave, Lane<D>((unsigned)(p.Hkv * D * 2), wave).vb0());
+    step_tile<D, 0, kExt, kKS>(ws, p, tp, wi, st, cur, t, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave,
+                               Lane<D>((unsigned)(p.Hkv * D * 2), wave).vb0());
+    step_tile<D, 1, kExt, kKS>(ws, p, tp, wi, st, cur, t + 1, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave,
+                               Lane<D>((unsigned)(p.Hkv * D * 2), wave).vb0());
   }
   if (t < tend)
-    step_tile<D, 0, kExt, kKS>(ws, p, tp, wi, st, cur, t, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave, Lane<D>((unsigned)(p.Hkv * D * 2), wave).vb0());
+    step_tile<D, 0, kExt, kKS>(ws, p, tp, wi, st, cur, t, te, phase, kbuf, vbuf, row_lo, row_hi, lane, wave,
+                               Lane<D>((unsigned)(p.Hkv * D * 2), wave).vb0());
 }
 
 // The kernel above: four waves (256 query rows, 64 per wave) walk every key
@@ -499,7 +505,8 @@ void attn_step_bf16_kernel(StepParams p) {
     step_tile<D, 1, kExt, false>(ws, p, tp, wi, st, cur, t + 1, tp.n, 0u, kbuf, vbuf, row_lo, row_hi, lane,
                                   wave, vb0);
   }
-  if (t < tp.n) step_tile<D, 0, kExt, false>(ws, p, tp, wi, st, cur, t, tp.n, 0u, kbuf, vbuf, row_lo, row_hi, lane, wave, vb0);
+  if (t < tp.n)
+    step_tile<D, 0, kExt, false>(ws, p, tp, wi, st, cur, t, tp.n, 0u, kbuf, vbuf, row_lo, row_hi, lane, wave, vb0);
 
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
