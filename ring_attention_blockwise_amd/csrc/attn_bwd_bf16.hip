@@ -1174,22 +1174,17 @@ template <bool kExt>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_kvb_kernel(BwdParams bp) {
   const StepParams& p = bp.s;
-  __shared__ __attribute__((aligned(16))) char q0_raw[kTileB];
-  __shared__ __attribute__((aligned(16))) char q1_raw[kTileB];
-  __shared__ __attribute__((aligned(16))) char q2_raw[kTileB];
-  __shared__ __attribute__((aligned(16))) char d0_raw[kTileB];
-  __shared__ __attribute__((aligned(16))) char d1_raw[kTileB];
-  __shared__ __attribute__((aligned(16))) char d2_raw[kTileB];
-  __shared__ __attribute__((aligned(16))) char l0_raw[768];  // L, -delta, and with masks the rows' key ranges
-  __shared__ __attribute__((aligned(16))) char l1_raw[768];
-  __shared__ __attribute__((aligned(16))) char l2_raw[768];
-  __shared__ __attribute__((aligned(16))) char p0_raw[kTileB];      // P: 4 waves x 2 halves x 1 KB
-  __shared__ __attribute__((aligned(16))) char p1_raw[kTileB];
-  __shared__ __attribute__((aligned(16))) char g0_raw[4 * 4096];    // dP - delta: 4 waves x 4 KB
-  __shared__ __attribute__((aligned(16))) char g1_raw[4 * 4096];
-  RA_LDS char* const lbuf[3] = {(RA_LDS char*)l0_raw, (RA_LDS char*)l1_raw, (RA_LDS char*)l2_raw};
-  RA_LDS char* const pbuf[2] = {(RA_LDS char*)p0_raw, (RA_LDS char*)p1_raw};
-  RA_LDS char* const gbuf[2] = {(RA_LDS char*)g0_raw, (RA_LDS char*)g1_raw};
+  // One array with fixed offsets: the Q, dO and L / -delta stages (the
+  // transposing and operand reads of every tile) below 64 KB, where a DS
+  // instruction's 16-bit offset reaches them from a per-lane base; then P
+  // (4 waves x 2 halves x 1 KB per stage) and dP - delta (4 waves x 4 KB).
+  constexpr int kQ = 0, kDo = 3 * kTileB, kL = 6 * kTileB, kP = kL + 3 * 768, kG = kP + 2 * kTileB;
+  static_assert(kL + 3 * 768 <= 65536, "staged tiles within reach of the DS offset");
+  __shared__ __attribute__((aligned(16))) char lds_raw[kG + 2 * 4 * 4096];
+  RA_LDS char* const lds = (RA_LDS char*)lds_raw;
+  RA_LDS char* const lbuf[3] = {lds + kL, lds + kL + 768, lds + kL + 1536};
+  RA_LDS char* const pbuf[2] = {lds + kP, lds + kP + kTileB};
+  RA_LDS char* const gbuf[2] = {lds + kG, lds + kG + 4 * 4096};
   const unsigned lane = threadIdx.x & 63u;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wave = wv & 3;  // the wave's 32 keys within the tile
@@ -1214,7 +1209,7 @@ void attn_bwd_kvb_kernel(BwdParams bp) {
   cur.first(p, qp, it.g, stg.row_bytes, kwg);
 
   if (!dv) {
-    RA_LDS char* const qbuf[3] = {(RA_LDS char*)q0_raw, (RA_LDS char*)q1_raw, (RA_LDS char*)q2_raw};
+    RA_LDS char* const qbuf[3] = {lds + kQ, lds + kQ + kTileB, lds + kQ + 2 * kTileB};
     KvbDk st;
     const uint16_t* kr = (const uint16_t*)((const char*)p.k + ro);
 #pragma unroll
@@ -1260,7 +1255,7 @@ void attn_bwd_kvb_kernel(BwdParams bp) {
     return;
   }
 
-  RA_LDS char* const dbuf[3] = {(RA_LDS char*)d0_raw, (RA_LDS char*)d1_raw, (RA_LDS char*)d2_raw};
+  RA_LDS char* const dbuf[3] = {lds + kDo, lds + kDo + kTileB, lds + kDo + 2 * kTileB};
   KvbDv st;
   const uint16_t* vr = (const uint16_t*)((const char*)p.v + ro);
 #pragma unroll
