@@ -771,9 +771,10 @@ void attn_bwd_kv_kernel(BwdParams bp) {
 // wave groups of a key tile (128 keys; waves w and w + 4 share keys 32w ..
 // 32w + 31).  Iteration t of the query-tile list:
 //   dK waves: S(t) = Q K^T, P(t) = exp2(S sl2 - L log2 e), P(t) to LDS as
-//     bf16 (the dV product's operand) and kept in float32 registers; then,
+//     bf16 (the dV product's operand) and kept in float32 registers; and,
 //     for tile t - 1, dS = P (dP - delta) with dP - delta from the dV waves,
-//     and dK^T += Q^T dS.
+//     and dK^T += Q^T dS (when both tiles are live and unmasked, P(t)'s
+//     vector work runs between these products).
 //   dV waves: dP(t) - delta = dO V^T - delta (the product chain starts from
 //     the staged -delta), to LDS as float32; then, for tile t - 1, dV^T +=
 //     dO^T P with P from the dK waves.
@@ -1047,12 +1048,58 @@ __device__ inline void kvb_dk_iter(KvbDk& st, const BwdParams& bp, const QPlan& 
         probabilities(KvbSel<false>{});
       else
         probabilities(KvbSel<true>{});
-    } else {
+    } else if (!(t > 0 && st.live_prev)) {
       probabilities(KvbSel<false>{});
+    } else {
+      // Both tiles live (unmasked kernel): tile t's P and tile t - 1's dK
+      // products in one stretch.  Per 16-row half: the half's operand reads
+      // (Q^T of tile t - 1, dP - delta, L), dS of tile t - 1, then its four
+      // products with the half's exponentials between them (the scheduler
+      // told one product, then seven vector instructions), so that the
+      // products run while this wave works through P.
+      const RA_LDS f32x4* g = (const RA_LDS f32x4*)(gbuf[PP] + wave * 4096) + lane;
+      unsigned b0, b1;
+      tr_bases(lane, b0, b1);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 g0 = g[(2 * hf) * 64], g1 = g[(2 * hf + 1) * 64];
+        const f32x4 l0 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L);
+        const f32x4 l1 = *(const RA_LDS f32x4*)(lt + 16 * hf + 8 * L + 4);
+        bf16x8 qt[kD / 32];
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+          qt[db] = tr_read(qbuf[PRV], (b0 ^ (64u * db)) + 16u * kRowB * hf, (b1 ^ (64u * db)) + 16u * kRowB * hf);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x8 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = st.pk[PP][8 * hf + e] * g0[e];
+          x[e + 4] = st.pk[PP][8 * hf + 4 + e] * g1[e];
+        }
+        const bf16x8 xb = __builtin_convertvector(x, bf16x8);
+        __builtin_amdgcn_sched_barrier(0);
+        const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+        f32x8 xp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hf + e], p.sl2, -lv[e] * kLog2e));
+          pk[8 * hf + e] = xp[e];
+        }
+        *(RA_LDS bf16x8*)(pbuf[PC] + (wave * 2 + hf) * 1024 + lane * 16) = __builtin_convertvector(xp, bf16x8);
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+          st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[db], xb, st.acc[db], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kD / 32; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (t > 0 && st.live_prev) {
+  if (t > 0 && st.live_prev && (kExt || !live)) {
     // dS of tile t - 1 from its P (kept) and dP - delta (the dV waves'),
     // then dK^T += Q^T dS over its two 16-row halves
     const RA_LDS f32x4* g = (const RA_LDS f32x4*)(gbuf[PP] + wave * 4096) + lane;
