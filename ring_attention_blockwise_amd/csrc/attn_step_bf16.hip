@@ -21,11 +21,12 @@
 //   * Keys are processed in tiles of 32, double-buffered in LDS.  Both tiles
 //     are copied global -> LDS by the load unit itself (buffer loads with the
 //     LDS bit, 16 bytes per lane), so staging takes no registers and no LDS
-//     store instructions.  Tile t+1 is started at the top of iteration t and
-//     waited for just before the barrier that ends it, so its latency hides
-//     behind a whole tile of work.  The per-tile bookkeeping (which rows the
-//     next tile holds, where they are) advances a small scalar cursor; the
-//     per-lane DMA offsets are computed once per work item.
+//     store instructions.  Tile t+1 is started early in iteration t (after
+//     the first four score products are issued) and waited for just before
+//     the barrier that ends it, so its latency hides behind a tile of work.
+//     The per-tile bookkeeping (which rows the next tile holds, where they
+//     are) advances a small scalar cursor; the per-lane DMA offsets are
+//     computed once per work item.
 //   * Only key tiles with at least one visible key are visited; tiles all of
 //     whose keys every row of the work item sees run first and skip the mask.
 //   * Steps with fewer work items than two per CU (small rings) run a
