@@ -298,6 +298,12 @@ __device__ inline void step_tile(WaveState<D>& ws, const StepParams& p, const Ti
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.q[qb][u], s[qb], 0, 0, 0);
   }
+  // Scheduling groups kept from the form that issued all sixteen products in
+  // this block: they name four products more than the twelve left here, and
+  // the scheduler places each later operand read just before its pair (one
+  // read in flight).  A pattern that matches the block (read, then its two
+  // products) was 0.3-0.6% slower, and reading one operand ahead gained
+  // nothing: the other wave of the SIMD covers these LDS round trips.
 #pragma unroll
   for (int u = 2; u < D / 16; ++u) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
