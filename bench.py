@@ -215,9 +215,14 @@ def time_launches(ra, w, rank, steps):
     return out
 
 
-def sample_clock(ra, w, rank, seconds=1.5):
-    """GFX clock (MHz) sampled with amd-smi while the same ring runs back to
-    back for about ``seconds``; None where amd-smi is not available."""
+def sample_clock(ra, w, rank, seconds=1.5, settle=0.5):
+    """GFX clocks (MHz) of the 8 XCDs, sampled with amd-smi while the same
+    ring runs back to back for about ``seconds`` after ``settle`` seconds of
+    the same load (the metrics lag: right after idle they still read the idle
+    boost clock).  ``current_gfxclk`` is the first XCD's alone and the XCDs
+    differ by up to ~7% under load, so each sample takes the mean and the
+    minimum over ``current_gfxclks``; a launch ends with its slowest XCD.
+    None where amd-smi is not available."""
     import threading
     import torch
     try:
@@ -227,15 +232,18 @@ def sample_clock(ra, w, rank, seconds=1.5):
     except Exception:          # noqa: BLE001 - the clock is a report, not a result
         return None
     q, ks, vs, o, lse = build_inputs(ra, w, rank)
-    samples, stop = [], threading.Event()
+    samples, stop, record = [], threading.Event(), threading.Event()
 
     def poll():
         while not stop.is_set():
             try:
                 m = amdsmi.amdsmi_get_gpu_metrics_info(h)
-                c = m.get("current_gfxclk")
-                if isinstance(c, (int, float)) and 0 < c < 10000:
-                    samples.append(float(c))
+                cs = m.get("current_gfxclks")
+                if not isinstance(cs, (list, tuple)):
+                    cs = [m.get("current_gfxclk")]
+                cs = [float(c) for c in cs if isinstance(c, (int, float)) and 0 < c < 10000]
+                if cs and record.is_set():
+                    samples.append((sum(cs) / len(cs), min(cs), len(cs)))
             except Exception:  # noqa: BLE001
                 pass
             stop.wait(0.02)
@@ -243,7 +251,9 @@ def sample_clock(ra, w, rank, seconds=1.5):
     t = threading.Thread(target=poll)
     t0 = time.perf_counter()
     t.start()
-    while time.perf_counter() - t0 < seconds:
+    while time.perf_counter() - t0 < settle + seconds:
+        if time.perf_counter() - t0 >= settle:
+            record.set()
         for _ in range(20):
             ra.ra_rank_forward(q, ks, vs, o, lse, S=w.S, P=w.P, rank=rank, order=w.order, causal=w.causal,
                                scale=w.scale)
@@ -258,9 +268,12 @@ def sample_clock(ra, w, rank, seconds=1.5):
     torch.cuda.empty_cache()
     if not samples:
         return None
-    samples.sort()
-    return {"gfxclk_mhz_median": samples[len(samples) // 2], "gfxclk_mhz_min": samples[0],
-            "gfxclk_mhz_max": samples[-1], "samples": len(samples), "source": "amdsmi current_gfxclk"}
+    means = sorted(x[0] for x in samples)
+    mins = sorted(x[1] for x in samples)
+    return {"gfxclk_mhz_median": round(means[len(means) // 2], 1), "gfxclk_mhz_min": round(means[0], 1),
+            "gfxclk_mhz_max": round(means[-1], 1), "slowest_xcd_mhz_median": round(mins[len(mins) // 2], 1),
+            "xcds": samples[0][2], "samples": len(samples),
+            "source": "amdsmi current_gfxclks, mean over the XCDs per sample, after the load settled"}
 
 
 def time_allgather(ra, w, rank, ring_ms, reps=5):
